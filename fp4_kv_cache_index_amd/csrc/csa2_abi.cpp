@@ -1,0 +1,134 @@
+// Host side of the C-ABI declared in include/csa2.h: argument validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Every check here runs
+// before anything is enqueued, so a call that fails enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxCapacity = 2048LL * csa2::kFullChunk;  // chunk lists one merge accepts
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_cache(const csa2_cache* c, bool need_index, bool need_main) {
+  if (!c) return CSA2_EINVAL;
+  if (c->batch < 0 || c->capacity < 0) return CSA2_EINVAL;
+  if (c->ratio != 1 && c->ratio != 2) return CSA2_EINVAL;
+  if (c->capacity > kMaxCapacity) return CSA2_EUNSUPPORTED;
+  if (c->batch == 0) return CSA2_OK;
+  if (!c->length || !aligned(c->length, 4)) return CSA2_EINVAL;
+  if (need_index && (!c->ik_codes || !c->ik_scales || !aligned(c->ik_codes, 16) || !aligned(c->ik_scales, 4)))
+    return CSA2_EINVAL;
+  if (need_main && (!c->kv_codes || !c->kv_scales || !aligned(c->kv_codes, 16) || !aligned(c->kv_scales, 4)))
+    return CSA2_EINVAL;
+  return CSA2_OK;
+}
+
+csa2::LaunchCache to_launch(const csa2_cache* c) {
+  csa2::LaunchCache l;
+  l.kv_codes = c->kv_codes;
+  l.kv_scales = c->kv_scales;
+  l.ik_codes = c->ik_codes;
+  l.ik_scales = c->ik_scales;
+  l.length = c->length;
+  l.batch = c->batch;
+  l.capacity = c->capacity;
+  l.ratio = c->ratio;
+  return l;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int csa2_quantize_append(const csa2_cache* cache, const float* kv, const float* logits, const float* ik, int32_t T,
+                         int32_t host_len_bound, void* stream) {
+  int rc = check_cache(cache, true, true);
+  if (rc != CSA2_OK) return rc;
+  if (T < 0 || host_len_bound < 0) return CSA2_EINVAL;
+  if (T % cache->ratio != 0) return CSA2_EINVAL;
+  if ((cache->ratio == 2) != (logits != nullptr)) return CSA2_EINVAL;
+  const int64_t n_new = T / cache->ratio;
+  if ((int64_t)host_len_bound + n_new > cache->capacity) return CSA2_ECAPACITY;
+  if (cache->batch == 0 || T == 0) return CSA2_OK;
+  if (!kv || !ik || !aligned(kv, 16) || !aligned(ik, 4)) return CSA2_EINVAL;
+  if (logits && !aligned(logits, 4)) return CSA2_EINVAL;
+  return from_hip(csa2::launch_quant_append(to_launch(cache), kv, logits, ik, T, (hipStream_t)stream));
+}
+
+int csa2_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,
+                    void* stream) {
+  if (S < 1 || B < 0 || T < 0 || T > S) return CSA2_EINVAL;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (!swa || !x || !seq_len || !aligned(swa, 4) || !aligned(x, 16) || !aligned(seq_len, 4)) return CSA2_EINVAL;
+  return from_hip(csa2::launch_swa_append(swa, S, x, seq_len, B, T, (hipStream_t)stream));
+}
+
+int csa2_index_score_topk(const csa2_cache* cache, int mode, const float* iq, const float* iw, const int32_t* q_pos,
+                          const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int rc = check_cache(cache, true, false);
+  if (rc != CSA2_OK) return rc;
+  if (Q < 0) return CSA2_EINVAL;
+  if (mode == CSA2_FULL) {
+    if (pool_in) return CSA2_EINVAL;
+  } else if (mode == CSA2_REINDEX) {
+    if (pool_out) return CSA2_EINVAL;
+  } else {
+    return CSA2_EINVAL;
+  }
+  if (cache->batch == 0 || Q == 0) return CSA2_OK;
+  if (mode == CSA2_REINDEX && (!pool_in || !aligned(pool_in, 4))) return CSA2_EINVAL;
+  if (!iq || !topk_out || !aligned(iq, 4) || !aligned(topk_out, 4)) return CSA2_EINVAL;
+  if ((iw && !aligned(iw, 4)) || (q_pos && !aligned(q_pos, 4)) || (pool_out && !aligned(pool_out, 4)))
+    return CSA2_EINVAL;
+  const size_t need = csa2_workspace_bytes(CSA2_OP_INDEX, cache->batch, Q, cache->capacity);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  return from_hip(csa2::launch_index(to_launch(cache), mode, iq, iw, q_pos, pool_in, topk_out, pool_out, Q, ws,
+                                     (hipStream_t)stream));
+}
+
+int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, const uint8_t* swa, int32_t S, const uint16_t* q,
+                       const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_cache(cache, false, true);
+  if (rc != CSA2_OK) return rc;
+  if (Q < 0 || S < 1) return CSA2_EINVAL;
+  if (cache->batch == 0 || Q == 0) return CSA2_OK;
+  if (!topk || !swa || !q || !out) return CSA2_EINVAL;
+  if (!aligned(topk, 4) || !aligned(swa, 16) || !aligned(q, 16) || !aligned(out, 4)) return CSA2_EINVAL;
+  if ((lse && !aligned(lse, 4)) || (q_pos && !aligned(q_pos, 4))) return CSA2_EINVAL;
+  const size_t need = csa2_workspace_bytes(CSA2_OP_ATTEND, cache->batch, Q, cache->capacity);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  return from_hip(csa2::launch_attend(to_launch(cache), topk, swa, S, q, q_pos, sm_scale, out, lse, Q, ws,
+                                      (hipStream_t)stream));
+}
+
+size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t capacity) {
+  if (B <= 0 || Q <= 0 || capacity < 0) return 0;
+  const int64_t bq = (int64_t)B * Q;
+  if (op == CSA2_OP_INDEX) return csa2::index_ws_bytes(bq, capacity);
+  if (op == CSA2_OP_ATTEND) return csa2::attend_ws_bytes(bq);
+  return 0;
+}
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_EINVAL: return "invalid argument";
+    case CSA2_ECAPACITY: return "append exceeds cache capacity";
+    case CSA2_EWORKSPACE: return "workspace missing or too small";
+    case CSA2_EUNSUPPORTED: return "unsupported request";
+    case CSA2_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* csa2_version(void) { return "csa2-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Launch entry points of the gfx950 kernels behind the C-ABI.  Host-side
+// validation lives in csa2_abi.cpp; these functions only size grids and launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct LaunchCache {
+  uint8_t* kv_codes;
+  uint8_t* kv_scales;
+  uint8_t* ik_codes;
+  float* ik_scales;
+  int32_t* length;
+  int32_t batch;
+  int32_t capacity;
+  int32_t ratio;
+};
+
+// ---- indexer geometry
+constexpr int kFullChunk = 4096;     // entries scored per workgroup in a Full scan
+constexpr int kReindexChunk = 1024;  // pool slots scored per workgroup in a Reindex scan
+constexpr int kTopK = 512;
+constexpr int kPoolBlocks = 2048;
+constexpr int kBlock = 8;
+constexpr int kPool = kPoolBlocks * kBlock;
+
+inline int64_t full_chunks(int32_t capacity) { return ((int64_t)capacity + kFullChunk - 1) / kFullChunk; }
+inline int64_t reindex_chunks() { return kPool / kReindexChunk; }
+
+// Workspace of one index call, per (sequence, query): sorted candidate lists
+// of each chunk (u64 keys), their counts, and the sorted block lists for the pool.
+struct IndexWs {
+  uint64_t* lists;    // [BQ][chunks][512]
+  uint32_t* counts;   // [BQ][chunks]
+  uint64_t* blists;   // [BQ][chunks][chunk/8]
+  uint32_t* bcounts;  // [BQ][chunks]
+};
+size_t index_ws_bytes(int64_t bq, int32_t capacity);
+IndexWs index_ws_carve(void* ws, int64_t bq, int64_t chunks, int chunk);
+
+// ---- attention geometry
+constexpr int kAttnKeys = 640;  // 512 selected + 128 window
+constexpr int kAttnTile = 32;
+int attend_splits(int64_t bq);
+size_t attend_ws_bytes(int64_t bq);
+
+hipError_t launch_quant_append(const LaunchCache& c, const float* kv, const float* logits, const float* ik,
+                               int32_t T, hipStream_t stream);
+hipError_t launch_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,
+                             hipStream_t stream);
+hipError_t launch_index(const LaunchCache& c, int mode, const float* iq, const float* iw, const int32_t* q_pos,
+                        const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws,
+                        hipStream_t stream);
+hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, const uint8_t* swa, int32_t S,
+                         const uint16_t* q, const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse,
+                         int32_t Q, void* ws, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,118 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every symbol include/csa2.h declares, sizes workspaces, and rejects invalid
+arguments with the documented status before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import fp4_kv_cache_index_amd as csa
+    if not os.path.exists(csa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    csa.lib()
+    return csa
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(csa2_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(csa):
+    syms = declared_symbols()
+    assert set(syms) == set(csa.EXPORTS), syms
+    L = csa.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings_and_version(csa):
+    for code in (csa.OK, csa.EINVAL, csa.ECAPACITY, csa.EWORKSPACE, csa.EUNSUPPORTED, csa.EHIP):
+        assert csa.status_string(code) and csa.status_string(code) != "unknown status"
+    assert csa.status_string(12345) == "unknown status"
+    assert "gfx950" in csa.version()
+
+
+def test_workspace_sizes(csa):
+    ws = csa.workspace_bytes
+    assert ws(csa.OP_INDEX, 0, 1, 100) == 0 and ws(7, 1, 1, 100) == 0
+    a = ws(csa.OP_INDEX, 16, 1, 131072)
+    assert a > 0 and ws(csa.OP_INDEX, 32, 1, 131072) > a and ws(csa.OP_INDEX, 16, 1, 262144) > a
+    assert ws(csa.OP_ATTEND, 16, 1, 0) > 0
+    assert ws(csa.OP_ATTEND, 1, 512, 0) == 0  # enough queries: no split, no workspace
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def cache(csa, B=2, cap=100, ratio=1, **over):
+    c = csa.CacheStruct(FAKE, FAKE, FAKE, FAKE, FAKE, B, cap, ratio)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_append_rejections(csa):
+    L = csa.lib()
+    p = ctypes.c_void_p(FAKE)
+    q = L.csa2_quantize_append
+    assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=2)), p, p, p, 3, 0, None) == csa.EINVAL      # T % r
+    assert q(ctypes.byref(cache(csa, ratio=2)), p, None, p, 2, 0, None) == csa.EINVAL   # logits missing
+    assert q(ctypes.byref(cache(csa, ratio=1)), p, p, p, 2, 0, None) == csa.EINVAL      # logits given
+    assert q(ctypes.byref(cache(csa, cap=10)), p, None, p, 4, 7, None) == csa.ECAPACITY
+    assert q(ctypes.byref(cache(csa)), p, None, p, -1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, kv_codes=None)), p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, cap=1 << 30)), p, None, p, 1, 0, None) == csa.EUNSUPPORTED
+    assert q(ctypes.byref(cache(csa)), ctypes.c_void_p(FAKE + 4), None, p, 1, 0, None) == csa.EINVAL  # misaligned
+    assert q(ctypes.byref(cache(csa)), p, None, p, 0, 0, None) == csa.OK  # nothing to do
+
+
+def test_swa_rejections(csa):
+    L = csa.lib()
+    p = ctypes.c_void_p(FAKE)
+    s = L.csa2_swa_append
+    assert s(p, 0, p, p, 1, 1, None) == csa.EINVAL
+    assert s(p, 128, p, p, 1, 129, None) == csa.EINVAL
+    assert s(None, 128, p, p, 1, 1, None) == csa.EINVAL
+    assert s(p, 128, p, None, 1, 1, None) == csa.EINVAL
+    assert s(p, 128, p, p, 0, 1, None) == csa.OK
+
+
+def test_index_rejections(csa):
+    L = csa.lib()
+    p = ctypes.c_void_p(FAKE)
+    f = L.csa2_index_score_topk
+    c = ctypes.byref(cache(csa, cap=131072))
+    assert f(c, 5, p, None, None, None, p, None, 1, p, 1 << 40, None) == csa.EINVAL          # mode
+    assert f(c, csa.FULL, p, None, None, p, p, None, 1, p, 1 << 40, None) == csa.EINVAL      # pool_in on Full
+    assert f(c, csa.REINDEX, p, None, None, None, p, None, 1, p, 1 << 40, None) == csa.EINVAL  # no pool_in
+    assert f(c, csa.REINDEX, p, None, None, p, p, p, 1, p, 1 << 40, None) == csa.EINVAL     # pool_out on Reindex
+    assert f(c, csa.FULL, None, None, None, None, p, None, 1, p, 1 << 40, None) == csa.EINVAL
+    assert f(c, csa.FULL, p, None, None, None, p, None, 1, p, 16, None) == csa.EWORKSPACE
+    assert f(c, csa.FULL, p, None, None, None, p, None, 1, None, 0, None) == csa.EWORKSPACE
+    assert f(c, csa.FULL, p, None, None, None, p, None, -1, p, 1 << 40, None) == csa.EINVAL
+    big = ctypes.byref(cache(csa, cap=(1 << 23) + 1))
+    assert f(big, csa.FULL, p, None, None, None, p, None, 1, p, 1 << 40, None) == csa.EUNSUPPORTED
+    assert f(c, csa.FULL, p, None, None, None, p, None, 0, None, 0, None) == csa.OK
+
+
+def test_attend_rejections(csa):
+    L = csa.lib()
+    p = ctypes.c_void_p(FAKE)
+    a = L.csa2_sparse_attend
+    c = ctypes.byref(cache(csa, B=16))
+    assert a(c, p, p, 0, p, None, 1.0, p, None, 1, p, 1 << 40, None) == csa.EINVAL        # S
+    assert a(c, None, p, 128, p, None, 1.0, p, None, 1, p, 1 << 40, None) == csa.EINVAL   # topk
+    assert a(c, p, p, 128, p, None, 1.0, None, None, 1, p, 1 << 40, None) == csa.EINVAL   # out
+    assert a(c, p, p, 128, p, None, 1.0, p, None, 1, p, 8, None) == csa.EWORKSPACE
+    assert a(ctypes.byref(cache(csa, kv_scales=None)), p, p, 128, p, None, 1.0, p, None, 1, p, 1 << 40,
+             None) == csa.EINVAL

@@ -1,0 +1,376 @@
+"""GPU parity of every step of the CSA2 path against the CPU oracle.
+
+Each test builds seeded inputs, runs the C-ABI through the Python binding on
+the GPU, runs the oracle on the same inputs, and compares: codes bit-exact,
+Top-K / pool sets under the boundary rule, attention within 2e-3 + 1e-2|ref|.
+Where a stage consumes an upstream result, both sides get the same upstream
+(oracle-made) input so differences cannot cascade.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import attn_close, check_sorted_list, pool_block_swaps, topk_swaps
+
+pytestmark = pytest.mark.gpu
+SM = float(np.float32(1.0 / math.sqrt(512.0)))
+
+
+@pytest.fixture(scope="module")
+def csa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import fp4_kv_cache_index_amd as csa
+    csa.lib()  # raises if the HIP library is not built
+    return csa
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def special_rows(n):
+    """Rows mixing the hand-worked groups, saturation, zeros, signed zeros,
+    tiny and subnormal-scale groups, and Gaussian rows at many magnitudes."""
+    rows = synth.normal(11, "special", (n, 512)).astype(np.float32)
+    mags = np.exp(synth.uniform(11, "mags", (n, 32), -9.0, 9.0)).astype(np.float32)
+    rows = (rows.reshape(n, 32, 16) * mags[:, :, None]).reshape(n, 512)
+    if n > 0:
+        g = [[0.5, -1.0, 3.0, 2.9, 6.0, -6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.1, 0.0, -0.0],
+             [10.0, 1.0, -4.0, 0.8125, 2.4375, 3.25, 4.0625, 5.6875, 8.125, -10.0, 0.40625, 0.4, 1.21875, 0.0,
+              -2.0, 9.0],
+             [0.0] * 3 + [-0.0] + [0.0] * 12,
+             [0.003, -0.002, 0.001] + [0.0] * 13,
+             [0.03, 0.0146484375, -0.005859375] + [0.0] * 13,
+             [3000.0, -2688.0, 1344.0] + [0.0] * 13]
+        for i, grp in enumerate(g):
+            rows[0, 16 * i:16 * i + 16] = grp
+    if n > 1:
+        rows[1] = 0.0
+    if n > 2:
+        rows[2] = -rows[2] * 1e5  # saturating everywhere
+    return rows
+
+
+# ------------------------------------------------------------------ append
+@pytest.mark.parametrize("B,T,ratio,pre", [(1, 1, 1, 0), (3, 5, 1, 7), (2, 64, 1, 0), (1, 300, 1, 5),
+                                           (2, 8, 2, 3), (1, 2048, 2, 0)])
+def test_quantize_append_bitexact(csa, orc, B, T, ratio, pre):
+    n_new = T // ratio
+    cap = pre + n_new + 3
+    kv = special_rows(B * T).reshape(B, T, 512)
+    ik = synth.normal(12, f"ik{T}", (B, n_new, 64)) * np.float32(3.0)
+    ik[0, 0] = 0.0
+    logits = synth.normal(12, f"lg{T}", (B, T, 512)) * np.float32(2.0) if ratio == 2 else None
+    oc = orc.Cache(B, cap, ratio)
+    oc.length[:] = pre
+    orc.quantize_append(oc, kv, ik, logits=logits)
+
+    gc = csa.Cache(B, cap, ratio)
+    gc.length.fill_(pre)
+    gc.host_len_bound = pre
+    csa.quantize_append(gc, dev(kv), dev(ik), logits=dev(logits) if logits is not None else None)
+    assert np.array_equal(host(gc.length), oc.length)
+    assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
+    assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
+    assert np.array_equal(host(gc.ik_codes), oc.ik_codes)
+    assert np.array_equal(host(gc.ik_scales).view(np.uint32), oc.ik_scales.view(np.uint32))
+
+
+def test_quantize_append_capacity(csa):
+    gc = csa.Cache(2, 10, 1)
+    kv = dev(synth.normal(13, "kv", (2, 4, 512)))
+    ik = dev(synth.normal(13, "ik", (2, 4, 64)))
+    gc.host_len_bound = 8
+    with pytest.raises(csa.CSA2Error) as ei:
+        csa.quantize_append(gc, kv, ik)
+    assert ei.value.status == csa.ECAPACITY
+    # device guard: the host bound lies, sequence 1 is already full
+    gc.length.copy_(torch.tensor([2, 9], dtype=torch.int32))
+    gc.host_len_bound = 0
+    csa.quantize_append(gc, kv, ik)
+    assert host(gc.length).tolist() == [6, 9]
+    assert not host(gc.kv_codes)[1].any()
+
+
+# ------------------------------------------------------------------ window
+@pytest.mark.parametrize("B,S,T", [(1, 128, 1), (3, 128, 5), (2, 300, 128), (2, 2175, 2048)])
+def test_swa_append_bitexact(csa, orc, B, S, T):
+    seq = np.array([T + 17 * b + (S if b == 1 else 0) for b in range(B)], np.int32)
+    x = special_rows(B * T).reshape(B, T, 512)
+    ref = np.zeros((B, S, 512), np.uint8)
+    orc.swa_append(ref, x, seq)
+    g = torch.zeros((B, S, 512), dtype=torch.uint8, device="cuda")
+    csa.swa_append(g, dev(x), dev(seq))
+    assert np.array_equal(host(g), ref)
+
+
+# ------------------------------------------------------------------ index
+def oracle_cache_ik(orc, B, cap, lengths, cid, ratio=1, tag="ik"):
+    oc = orc.Cache(B, cap, ratio)
+    for b in range(B):
+        n = int(lengths[b])
+        k = synth.normal_rows(cid, tag, b * cap, n, 64)
+        oc.ik_codes[b, :n], oc.ik_scales[b, :n] = orc.quantize_ik(k)
+        oc.length[b] = n
+    return oc
+
+
+def upload(csa, oc, with_main=False):
+    gc = csa.Cache(oc.B, oc.cap, oc.ratio)
+    gc.ik_codes.copy_(dev(oc.ik_codes))
+    gc.ik_scales.copy_(dev(oc.ik_scales))
+    gc.length.copy_(dev(oc.length))
+    if with_main:
+        gc.kv_codes.copy_(dev(oc.kv_codes))
+        gc.kv_scales.copy_(dev(oc.kv_scales))
+    gc.host_len_bound = int(oc.length.max()) if oc.B else 0
+    return gc
+
+
+def run_full(csa, gc, iq, q_pos=None, want_pool=True):
+    B, Q = iq.shape[0], iq.shape[1]
+    topk = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
+    pool = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device="cuda") if want_pool else None
+    csa.index_score_topk(gc, csa.FULL, dev(iq), topk, q_pos=dev(q_pos) if q_pos is not None else None,
+                         pool_out=pool)
+    return host(topk), host(pool) if want_pool else None
+
+
+@pytest.mark.parametrize("E", [1, 7, 8, 9, 511, 512, 513, 4095, 4096, 4097, 16383, 16384, 16385, 40000])
+def test_index_full_topk_and_pool(csa, orc, E):
+    B = 2
+    cap = E + 5
+    lengths = [E, max(1, E // 2)]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 20)
+    iq = synth.normal(20, f"iq{E}", (B, 1, 4, 64))
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq)
+    swaps = 0
+    for b in range(B):
+        swaps += topk_swaps(topk[b, 0], ref_topk[b, 0], scores[b, 0], name=f"topk b{b}")
+        swaps += pool_block_swaps(pool[b, 0], ref_pool[b, 0], scores[b, 0], lengths[b], name=f"pool b{b}")
+    print(f"E={E}: boundary swaps {swaps}")
+
+
+def test_index_full_multiquery_causal_ratio2(csa, orc):
+    B, E, ratio = 2, 5000, 2
+    cap = 5003
+    oc = oracle_cache_ik(orc, B, cap, [E, 3001], 21, ratio=ratio)
+    q_pos = np.array([[0, 1, 2, 3, 1023, 1024, 4095, 9999, 10005],
+                      [5, 6, 600, 601, 2047, 6001, 6002, 6003, 100]], np.int32)
+    Q = q_pos.shape[1]
+    iq = synth.normal(21, "iq", (B, Q, 4, 64))
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq, q_pos=q_pos)
+    for b in range(B):
+        for q in range(Q):
+            n_vis = min(int(oc.length[b]), (int(q_pos[b, q]) + 1) // ratio)
+            topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"topk b{b} q{q}")
+            pool_block_swaps(pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
+
+
+def test_index_relu_zero_ties_exact(csa, orc):
+    B, E = 1, 9000
+    oc = orc.Cache(B, E, 1)
+    k = np.abs(synth.normal_rows(22, "pos", 0, E, 64)) + 0.1
+    oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
+    oc.length[0] = E
+    iq = -np.abs(synth.normal(22, "neg", (1, 1, 4, 64))) - 0.1
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq)
+    assert np.array_equal(topk[0, 0], np.arange(512))
+    assert np.array_equal(pool[0, 0][:E], np.arange(E)) and np.all(pool[0, 0][E:] == -1)
+
+
+def test_index_weights_and_needles(csa, orc):
+    B, E = 1, 70000
+    iq = synth.normal(23, "iq", (1, 1, 4, 64))
+    k = synth.normal_rows(23, "k", 0, E, 64) * np.float32(0.05)
+    needles = np.unique(synth.integers(23, "pos", (300,), 0, E))
+    direction = np.maximum(iq[0, 0], 0).sum(axis=0) + 1e-3
+    k[needles] = direction / np.abs(direction).max() * 3.0
+    oc = orc.Cache(B, E, 1)
+    oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
+    oc.length[0] = E
+    iw = np.array([[[0.5, 2.0, 1.0, 0.25]]], np.float32)
+    ref, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, iw=iw, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk = torch.empty((1, 1, 512), dtype=torch.int32, device="cuda")
+    pool = torch.empty((1, 1, csa.POOL), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.FULL, dev(iq), topk, iw=dev(iw), pool_out=pool)
+    topk, pool = host(topk), host(pool)
+    topk_swaps(topk[0, 0], ref[0, 0], scores[0, 0])
+    pool_block_swaps(pool[0, 0], ref_pool[0, 0], scores[0, 0], E)
+    assert set(needles.tolist()) <= set(topk[0, 0].tolist())
+
+
+@pytest.mark.parametrize("E", [3000, 16384, 50000])
+def test_index_reindex(csa, orc, E):
+    B = 3
+    cap = E
+    lengths = [E, E - 7, max(1, E // 3)]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 24)
+    iq_full = synth.normal(24, f"f{E}", (B, 1, 4, 64))
+    _, pool, _ = orc.index_topk(oc, orc.FULL, iq_full, want_pool=True)
+    iq = synth.normal(24, f"r{E}", (B, 1, 4, 64))
+    ref, _, scores = orc.index_topk(oc, orc.REINDEX, iq, pool_in=pool, want_scores=True)
+    gc = upload(csa, oc)
+    topk = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.REINDEX, dev(iq), topk, pool_in=dev(pool))
+    topk = host(topk)
+    for b in range(B):
+        topk_swaps(topk[b, 0], ref[b, 0], scores[b, 0], name=f"reindex b{b}")
+        assert set(topk[b, 0][topk[b, 0] >= 0].tolist()) <= set(pool[b, 0].tolist())
+    # Reindex with the Full layer's own queries reproduces the Full Top-512
+    ref_full, _, _ = orc.index_topk(oc, orc.FULL, iq_full)
+    t = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.REINDEX, dev(iq_full), t, pool_in=dev(pool))
+    got = host(t)
+    for b in range(B):
+        assert set(got[b, 0].tolist()) == set(ref_full[b, 0].tolist())
+
+
+def test_index_deterministic(csa, orc):
+    B, E = 2, 30000
+    oc = oracle_cache_ik(orc, B, E, [E, E], 25)
+    gc = upload(csa, oc)
+    iq = synth.normal(25, "iq", (B, 1, 4, 64))
+    a = run_full(csa, gc, iq)
+    b = run_full(csa, gc, iq)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ attention
+def oracle_cache_full(orc, B, cap, lengths, cid, ratio=1):
+    oc = orc.Cache(B, cap, ratio)
+    for b in range(B):
+        n = int(lengths[b])
+        kv = synth.normal_rows(cid, "kv", b * cap, n, 512)
+        oc.kv_codes[b, :n], oc.kv_scales[b, :n] = orc.quantize_main(kv)
+        k = synth.normal_rows(cid, "ik", b * cap, n, 64)
+        oc.ik_codes[b, :n], oc.ik_scales[b, :n] = orc.quantize_ik(k)
+        oc.length[b] = n
+    return oc
+
+
+def bf16_round(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,Q,E,S,mode", [
+    (1, 1, 40, 128, "decode"),        # few entries: most Top-K slots are -1, p < 127
+    (2, 1, 5000, 128, "decode"),      # multi-split decode
+    (3, 2, 9000, 256, "qpos"),        # explicit positions, ring larger than the window
+    (1, 300, 4000, 512, "prefill"),   # single-split path (B*Q >= 256)
+    (2, 3, 0, 128, "empty"),          # no global entries, window only
+])
+def test_attend(csa, orc, B, Q, E, S, mode):
+    cap = max(E, 1) + 3
+    lengths = [E] * B
+    oc = oracle_cache_full(orc, B, cap, lengths, 30)
+    if mode == "qpos":
+        q_pos = np.array([[E - 1, E - 100][:Q] for _ in range(B)], np.int32)
+    elif mode == "prefill":
+        q_pos = np.array([[E - Q + q for q in range(Q)] for _ in range(B)], np.int32)
+    else:
+        q_pos = None
+    pos_last = (q_pos.max(axis=1) if q_pos is not None else np.array(lengths) - 1).astype(np.int64)
+    if E > 0:
+        iq = synth.normal(30, "iq", (B, Q, 4, 64))
+        topk, _, _ = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos)
+    else:
+        # window only: one sequence shorter than the window, one longer
+        topk = np.full((B, Q, 512), -1, np.int32)
+        pos_last = np.array([5, 200] * B, np.int64)[:B]
+        q_pos = np.array([[int(pos_last[b]) - (Q - 1 - q) for q in range(Q)] for b in range(B)], np.int32)
+    # window ring: fill positions up to each sequence's last query position
+    swa = np.zeros((B, S, 512), np.uint8)
+    for b in range(B):
+        n_tok = int(pos_last[b]) + 1
+        t0 = max(0, n_tok - S)
+        x = synth.normal_rows(30, "swa", b * 100000 + t0, n_tok - t0, 512).reshape(1, -1, 512)
+        sub = np.zeros((1, S, 512), np.uint8)
+        orc.swa_append(sub, x, np.array([n_tok], np.int32))
+        swa[b] = sub[0]
+    qf = bf16_round(synth.normal(30, "q", (B, Q, 16, 512)))
+    ref, ref_lse = orc.attend(oc, topk, swa, qf.float().numpy(), SM, q_pos=q_pos)
+
+    gc = upload(csa, oc, with_main=True)
+    out = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Q, 16), dtype=torch.float32, device="cuda")
+    csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out, SM, lse=lse,
+                      q_pos=dev(q_pos) if q_pos is not None else None)
+    got = host(out.float())
+    mabs, mrel = attn_close(got, ref)
+    got_lse = host(lse)
+    np.testing.assert_allclose(got_lse, ref_lse, rtol=1e-4, atol=1e-4)
+    print(f"attend {mode}: max abs {mabs:.2e}, max rel {mrel:.2e}")
+    # deterministic
+    out2 = torch.empty_like(out)
+    csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out2, SM, q_pos=dev(q_pos) if q_pos is not None else None)
+    assert torch.equal(out, out2)
+
+
+# ------------------------------------------------------------------ step
+def test_decode_group_step_small(csa, orc):
+    """Full(+pool) -> Reindex -> Reuse -> Reuse decode steps on a small cache,
+    GPU and oracle each running the whole schedule from the same fp32 inputs."""
+    B, E0, cap, S, steps = 2, 20000, 20010, 128, 3
+    lengths = [E0, E0 - 3000]
+    oc = oracle_cache_full(orc, B, cap, lengths, 40)
+    gc = upload(csa, oc, with_main=True)
+    swa_o = [np.zeros((B, S, 512), np.uint8) for _ in range(4)]
+    for l in range(4):
+        for b in range(B):
+            n = lengths[b]
+            x = synth.normal_rows(40, f"swa{l}", b * 100000 + n - S, S, 512).reshape(1, S, 512)
+            sub = np.zeros((1, S, 512), np.uint8)
+            orc.swa_append(sub, x, np.array([n], np.int32))
+            swa_o[l][b] = sub[0]
+    swa_g = [dev(s) for s in swa_o]
+    for step in range(steps):
+        kv = synth.normal(41, f"kv{step}", (B, 1, 512))
+        ik = synth.normal(41, f"ik{step}", (B, 1, 64))
+        orc.quantize_append(oc, kv, ik)
+        csa.quantize_append(gc, dev(kv), dev(ik))
+        assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
+        seq_o = oc.length.copy()
+        topk_prev = None
+        pool_o = None
+        for l, mode in enumerate(("full_pool", "reindex", "reuse", "reuse")):
+            xs = synth.normal(42, f"x{step}_{l}", (B, 1, 512))
+            orc.swa_append(swa_o[l], xs, seq_o)
+            csa.swa_append(swa_g[l], dev(xs), gc.length)
+            assert np.array_equal(host(swa_g[l]), swa_o[l])
+            iq = synth.normal(43, f"iq{step}_{l}", (B, 1, 4, 64))
+            if mode == "full_pool":
+                ref, pool_o, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+                g_topk, g_pool = run_full(csa, gc, iq)
+                for b in range(B):
+                    topk_swaps(g_topk[b, 0], ref[b, 0], scores[b, 0])
+                    pool_block_swaps(g_pool[b, 0], pool_o[b, 0], scores[b, 0], int(oc.length[b]))
+                topk_prev = ref
+            elif mode == "reindex":
+                ref, _, scores = orc.index_topk(oc, orc.REINDEX, iq, pool_in=pool_o, want_scores=True)
+                t = torch.empty((B, 1, 512), dtype=torch.int32, device="cuda")
+                csa.index_score_topk(gc, csa.REINDEX, dev(iq), t, pool_in=dev(pool_o))
+                g = host(t)
+                for b in range(B):
+                    topk_swaps(g[b, 0], ref[b, 0], scores[b, 0])
+                topk_prev = ref
+            qf = bf16_round(synth.normal(44, f"q{step}_{l}", (B, 1, 16, 512)))
+            ref_o, _ = orc.attend(oc, topk_prev, swa_o[l], qf.float().numpy(), SM)
+            out = torch.empty((B, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+            csa.sparse_attend(gc, dev(topk_prev), swa_g[l], qf.cuda(), out, SM)
+            attn_close(host(out.float()), ref_o, name=f"step {step} layer {l}")
