@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the Full layer's FP4
+quantise-and-append of the new token, then for every layer of the group its
+window append, its indexing call (Full with pool, Reindex, or none for Reuse)
+and its attention.  The default workload is the decoder group Full(+pool) +
+Reindex + 2 Reuse over 16 sequences of 128K context.  Each step is captured
+once as a hipGraph per cache replica; three replicas rotate so that the
+256 MB Infinity Cache cannot keep the 143 MB of indexer K resident between
+steps.  Inputs are seeded synthetic N(0, 1) rows drawn on the device.
+
+Prints one JSON line: metric, value (layer-steps/s; one layer-step advances
+every sequence of the batch through one CSA2 layer), roofline of the dominant
+kernel (the Full indexer call, timed with HIP events on its stream), and the
+CPU oracle timed on the host as a correctness baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "CSA2 decode layer-steps/sec and achieved HBM GB/s (% of peak) at 128K ctx"
+UNIT = "layer-steps/s"
+PEAK_GBPS = 8000.0
+SM_SCALE = float(np.float32(1.0 / math.sqrt(512.0)))
+ROWS_PER_SEQ = 1 << 22          # row namespace of one sequence in the seeded generators
+FILL_FLOATS = 32 * 1024 * 1024  # fp32 values per cache-fill chunk
+MAIN_ROW, IDX_ROW, SWA_ROW = 288, 68, 512
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device state of one workload: R cache replicas, per-layer windows, inputs,
+    outputs and workspaces, and the step that runs the whole group."""
+
+    def __init__(self, cid, replicas, extra_steps, keep_host_seqs=0):
+        import fp4_kv_cache_index_amd as csa
+        self.csa = csa
+        w = synth.WORKLOADS[cid]
+        self.cid, self.name = cid, w["name"]
+        self.B, self.ctx, self.r, self.Q, self.group = w["B"], w["ctx"], w["ratio"], w["Q"], w["group"]
+        self.decode = self.Q == 1
+        self.L = len(self.group)
+        B, r, Q = self.B, self.r, self.Q
+        if self.decode:
+            self.E_before = self.ctx // r          # entries present before the step
+            self.T_step = 1                        # tokens appended per step
+            self.S = 128
+            cap = self.E_before + extra_steps + 16
+        else:
+            self.T_step = Q                        # the prefill chunk
+            self.E_before = (self.ctx - Q) // r
+            self.S = 128 + Q                       # ring holds every window of the chunk
+            cap = self.ctx // r + 16
+        self.cap = cap
+        dev = "cuda"
+        t0 = time.time()
+        self.caches = [csa.Cache(B, cap, r) for _ in range(replicas)]
+        c0 = self.caches[0]
+        # ---- fill replica 0 with the context, keep host rows for the oracle sample
+        self.host_rows = None
+        hs = min(keep_host_seqs, B)
+        if hs:
+            self.host_rows = dict(kv=np.empty((hs, self.E_before * r, 512), np.float32),
+                                  ik=np.empty((hs, self.E_before, 64), np.float32),
+                                  lg=np.empty((hs, self.E_before * r, 512), np.float32) if r == 2 else None)
+        T_fill = max(r, (FILL_FLOATS // (B * 512)) // r * r)
+        tok = 0
+        total_tok = self.E_before * r
+        while tok < total_tok:
+            T = min(T_fill, total_tok - tok)
+            kv = torch.stack([synth.torch_normal_rows(cid, "kv", b * ROWS_PER_SEQ + tok, T, 512) for b in range(B)])
+            ik = torch.stack([synth.torch_normal_rows(cid, "ik", b * ROWS_PER_SEQ + tok // r, T // r, 64)
+                              for b in range(B)])
+            lg = None
+            if r == 2:
+                lg = torch.stack([synth.torch_normal_rows(cid, "logit", b * ROWS_PER_SEQ + tok, T, 512)
+                                  for b in range(B)])
+            csa.quantize_append(c0, kv, ik, logits=lg)
+            if hs:
+                self.host_rows["kv"][:, tok:tok + T] = kv[:hs].cpu().numpy()
+                self.host_rows["ik"][:, tok // r:(tok + T) // r] = ik[:hs].cpu().numpy()
+                if r == 2:
+                    self.host_rows["lg"][:, tok:tok + T] = lg[:hs].cpu().numpy()
+            tok += T
+        torch.cuda.synchronize()
+        for c in self.caches[1:]:
+            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_scales", "length"):
+                getattr(c, name).copy_(getattr(c0, name))
+        for c in self.caches:
+            c.host_len_bound = self.E_before
+        log(f"filled {replicas} replica(s) of {B} x {self.E_before} entries in {time.time() - t0:.1f}s")
+
+        # ---- per-layer windows: the S tokens before the step, then the step's own tokens
+        tok_before = self.E_before * r
+        self.swa_rows = [torch.stack([synth.torch_normal_rows(cid, f"swa{l}", b * ROWS_PER_SEQ + tok_before - 128,
+                                                              128, 512) for b in range(B)]) for l in range(self.L)]
+        self.swas = []
+        seq_before = torch.full((B,), tok_before, dtype=torch.int32, device=dev)
+        for _ in range(replicas):
+            per = []
+            for l in range(self.L):
+                s = torch.zeros((B, self.S, 512), dtype=torch.uint8, device=dev)
+                csa.swa_append(s, self.swa_rows[l], seq_before)
+                per.append(s)
+            self.swas.append(per)
+        # ---- step inputs: one set per replica
+        self.seq_after = torch.full((B,), tok_before + self.T_step, dtype=torch.int32, device=dev)
+        self.q_pos = None
+        if not self.decode:
+            self.q_pos = (torch.arange(Q, dtype=torch.int32, device=dev) + tok_before).repeat(B, 1).contiguous()
+        self.inputs = []
+        for i in range(replicas):
+            g = f"step{i}"
+            inp = dict(
+                kv=torch.stack([synth.torch_normal_rows(cid, g + "kv", b * ROWS_PER_SEQ, self.T_step, 512)
+                                for b in range(B)]),
+                ik=torch.stack([synth.torch_normal_rows(cid, g + "ik", b * ROWS_PER_SEQ, self.T_step // r, 64)
+                                for b in range(B)]),
+                lg=(torch.stack([synth.torch_normal_rows(cid, g + "lg", b * ROWS_PER_SEQ, self.T_step, 512)
+                                 for b in range(B)]) if r == 2 else None),
+                x=[torch.stack([synth.torch_normal_rows(cid, g + f"x{l}", b * ROWS_PER_SEQ, self.T_step, 512)
+                                for b in range(B)]) for l in range(self.L)],
+                iq=[synth.torch_normal_rows(cid, g + f"iq{l}", 0, B * Q * 4, 64).reshape(B, Q, 4, 64).contiguous()
+                    for l in range(self.L)],
+                q=[synth.torch_normal_rows(cid, g + f"q{l}", 0, B * Q * 16, 512).reshape(B, Q, 16, 512)
+                   .to(torch.bfloat16).contiguous() for l in range(self.L)],
+            )
+            self.inputs.append(inp)
+        # ---- outputs and workspaces
+        self.topk = [torch.empty((B, Q, 512), dtype=torch.int32, device=dev) for _ in range(self.L)]
+        self.pool = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device=dev)
+        self.out = [torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device=dev) for _ in range(self.L)]
+        self.ws_idx = torch.zeros(max(1, csa.workspace_bytes(csa.OP_INDEX, B, Q, cap)), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_att = torch.zeros(max(1, csa.workspace_bytes(csa.OP_ATTEND, B, Q, cap)), dtype=torch.uint8,
+                                  device=dev)
+        torch.cuda.synchronize()
+
+    # one pass of the whole group on replica i
+    def step(self, i):
+        csa = self.csa
+        c, inp, swas = self.caches[i], self.inputs[i], self.swas[i]
+        if not self.decode:
+            c.length.fill_(self.E_before)
+        c.host_len_bound = self.E_before if not self.decode else c.host_len_bound
+        csa.quantize_append(c, inp["kv"], inp["ik"], logits=inp["lg"])
+        seq = c.length if (self.decode and self.r == 1) else self.seq_after
+        topk = None
+        for l, mode in enumerate(self.group):
+            csa.swa_append(swas[l], inp["x"][l], seq)
+            if mode in ("full", "full_pool"):
+                csa.index_score_topk(c, csa.FULL, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
+                                     pool_out=self.pool if mode == "full_pool" else None, ws=self.ws_idx)
+                topk = self.topk[l]
+            elif mode == "reindex":
+                csa.index_score_topk(c, csa.REINDEX, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
+                                     pool_in=self.pool, ws=self.ws_idx)
+                topk = self.topk[l]
+            csa.sparse_attend(c, topk, swas[l], inp["q"][l], self.out[l], SM_SCALE, q_pos=self.q_pos,
+                              ws=self.ws_att)
+
+    def full_index(self, i):
+        csa = self.csa
+        mode = self.group[0]
+        csa.index_score_topk(self.caches[i], csa.FULL, self.inputs[i]["iq"][0], self.topk[0], q_pos=self.q_pos,
+                             pool_out=self.pool if mode == "full_pool" else None, ws=self.ws_idx)
+
+    # algorithmic KV + indexer bytes of one step at E entries visible to the Full scan
+    def step_bytes(self, E):
+        B, Q, L = self.B, self.Q, self.L
+        n_sel = min(512, E)
+        by = 0
+        for mode in self.group:
+            if mode in ("full", "full_pool"):
+                by += B * E * IDX_ROW if self.decode else B * self.E_before * IDX_ROW
+            elif mode == "reindex":
+                by += B * min(16384, E) * IDX_ROW
+        by += L * B * Q * n_sel * MAIN_ROW
+        by += L * B * Q * 128 * SWA_ROW
+        return by
+
+
+def cpu_baseline(wl, steps=2):
+    """The oracle, as it stands, on the first sequences of the same workload."""
+    import oracle as orc
+    h = wl.host_rows
+    hs = h["kv"].shape[0]
+    r, B, Q = wl.r, wl.B, wl.Q
+    t0 = time.time()
+    oc = orc.Cache(hs, wl.cap, r)
+    orc.quantize_append(oc, h["kv"], h["ik"], logits=h["lg"])
+    swas = []
+    tok_before = wl.E_before * r
+    for l in range(wl.L):
+        s = np.zeros((hs, wl.S, 512), np.uint8)
+        orc.swa_append(s, wl.swa_rows[l][:hs].cpu().numpy(), np.full(hs, tok_before, np.int32))
+        swas.append(s)
+    inp = {k: (v[:hs].cpu().numpy() if isinstance(v, torch.Tensor) else
+               ([t[:hs].float().cpu().numpy() for t in v] if isinstance(v, list) else None))
+           for k, v in wl.inputs[0].items()}
+    q_pos = wl.q_pos[:hs].cpu().numpy() if wl.q_pos is not None else None
+    log(f"oracle sample set up in {time.time() - t0:.1f}s ({hs} sequences)")
+    times = []
+    for s_i in range(steps):
+        if not wl.decode:
+            oc.length[:] = wl.E_before
+        t = time.time()
+        orc.quantize_append(oc, inp["kv"], inp["ik"], logits=inp["lg"])
+        seq = oc.length * r if wl.decode else np.full(hs, tok_before + wl.T_step, np.int32)
+        topk, pool = None, None
+        for l, mode in enumerate(wl.group):
+            orc.swa_append(swas[l], inp["x"][l], seq.astype(np.int32))
+            if mode in ("full", "full_pool"):
+                topk, pool, _ = orc.index_topk(oc, orc.FULL, inp["iq"][l], q_pos=q_pos, want_pool=mode == "full_pool")
+            elif mode == "reindex":
+                topk, _, _ = orc.index_topk(oc, orc.REINDEX, inp["iq"][l], q_pos=q_pos, pool_in=pool)
+            orc.attend(oc, topk, swas[l], inp["q"][l], SM_SCALE, q_pos=q_pos)
+        times.append(time.time() - t)
+        log(f"oracle step {s_i}: {times[-1]:.2f}s")
+    t_step = float(np.median(times))
+    value = wl.L / t_step * hs / B
+    return dict(value=value, unit=UNIT, cores=int(min(orc.num_threads(), hs * Q)), kind="oracle",
+                sample=f"{steps} group steps of the first {hs} of {B} sequences (full context, all {wl.L} layers), "
+                       f"median {t_step:.2f}s per step, scaled by {B}/{hs} to the whole batch")
+
+
+def traffic_from_profiles(wl, kernel_name):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter
+    summaries, if they were taken on the kernel source as it is now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel_name}_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload preset (synth.WORKLOADS)")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: all)")
+    ap.add_argument("--roofline-iters", type=int, default=30)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build targets one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: run one process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    import fp4_kv_cache_index_amd as csa
+    csa.lib()
+    R = max(1, args.replicas)
+    extra = args.warmup + args.steps + 4 * R + 8
+    want_cpu = not args.no_cpu_baseline
+    wl0 = synth.WORKLOADS[args.config]
+    hs = (args.cpu_seqs or wl0["B"]) if want_cpu else 0
+    wl = Workload(args.config, R, extra, keep_host_seqs=hs)
+
+    # ---- capture one graph per replica
+    graphs = None
+    if not args.no_graph:
+        for i in range(R):  # eager warm-up outside capture
+            wl.step(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                wl.step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % R].replay()  # noqa: E731
+    else:
+        run = lambda i: wl.step(i % R)  # noqa: E731
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    E_start = int(wl.caches[0].length.max().item())
+    log(f"warm-up done, timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    E_end = int(wl.caches[0].length.max().item())
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.L * args.steps / wall
+    E_mid = (E_start + E_end) // 2 if wl.decode else wl.ctx // wl.r
+    step_bytes = wl.step_bytes(E_mid)
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step (events {gpu_ms * 1e3 / args.steps:.1f} us), {value:.0f} layer-steps/s, "
+        f"{step_gbps:.0f} GB/s on {step_bytes / 1e6:.1f} MB/step")
+
+    # ---- dominant kernel: the Full indexer call, HIP events on its stream
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.roofline_iters)]
+    for i in range(R):
+        wl.full_index(i)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)  # keep the GPU busy while the launches queue up
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        wl.full_index(i % R)
+        b.record(stream)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    t_idx = float(np.mean(durs))
+    E_idx = int(wl.caches[0].length.max().item()) if wl.decode else wl.ctx // wl.r
+    idx_bytes = wl.B * wl.Q * E_idx * IDX_ROW if wl.decode else wl.B * E_idx * IDX_ROW
+    achieved = idx_bytes / t_idx / 1e9
+    traffic = traffic_from_profiles(wl, "index_full")
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
+                frac=round(achieved / PEAK_GBPS, 4), traffic=traffic,
+                kernel="index_scan_kernel<4096> + index_merge_kernel (one csa2_index_score_topk Full call)",
+                bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
+    log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
+
+    cpu = None
+    if want_cpu:
+        cpu = cpu_baseline(wl)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context_tokens": wl.ctx, "ratio": wl.r,
+                   "queries_per_seq": wl.Q, "group": list(wl.group), "replicas": R,
+                   "hipgraph": graphs is not None},
+        "step_algorithmic_bytes": step_bytes, "step_GBps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / PEAK_GBPS, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

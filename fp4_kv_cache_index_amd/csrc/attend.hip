@@ -258,36 +258,43 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// One workgroup per (query, head): combine the splits' unnormalised partials by
+// their log-sum-exp weights; each thread owns two of the 512 output channels.
 __global__ void __launch_bounds__(kThreads)
     attend_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
                         int64_t bq_total, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float s_w[10][16];
-  __shared__ float s_lse[16];
+  __shared__ float s_m[16], s_l[16];
   const int64_t bq = blockIdx.x;
+  const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  if (tid < 16) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; s++) M = fmaxf(M, part_ml[((int64_t)s * bq_total + bq) * 32 + 2 * tid]);
-    float L = 0.0f;
-    for (int s = 0; s < splits; s++) {
-      const float m = part_ml[((int64_t)s * bq_total + bq) * 32 + 2 * tid];
-      const float l = part_ml[((int64_t)s * bq_total + bq) * 32 + 2 * tid + 1];
-      const float w = (m == -INFINITY) ? 0.0f : __expf(m - M);
-      s_w[s][tid] = w;
-      L += w * l;
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int s = 0; s < splits; s++) s_w[s][tid] *= inv;
-    s_lse[tid] = L > 0.0f ? M + __logf(L) : -INFINITY;
+  if (tid < splits) {
+    const float* pm = part_ml + ((int64_t)tid * bq_total + bq) * 32 + 2 * h;
+    s_m[tid] = pm[0];
+    s_l[tid] = pm[1];
   }
   __syncthreads();
-  for (int x = tid; x < 16 * 512; x += kThreads) {
-    const int h = x >> 9;
-    float o = 0.0f;
-    for (int s = 0; s < splits; s++) o += s_w[s][h] * part_o[((int64_t)s * bq_total + bq) * 16 * 512 + x];
-    out[bq * 16 * 512 + x] = f32_to_bf16_rne(o);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; s++) M = fmaxf(M, s_m[s]);
+  float L = 0.0f;
+  float w[10];
+#pragma unroll
+  for (int s = 0; s < 10; s++) {
+    w[s] = (s < splits && s_m[s] != -INFINITY) ? __expf(s_m[s] - M) : 0.0f;
+    L += s < splits ? w[s] * s_l[s] : 0.0f;
   }
-  if (lse && tid < 16) lse[bq * 16 + tid] = s_lse[tid];
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 10; s++) {
+    if (s < splits) {
+      const float2 v = *reinterpret_cast<const float2*>(part_o + (((int64_t)s * bq_total + bq) * 16 + h) * 512 + 2 * tid);
+      o0 += w[s] * v.x;
+      o1 += w[s] * v.y;
+    }
+  }
+  const uint32_t packed = (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16);
+  reinterpret_cast<uint32_t*>(out + (bq * 16 + h) * 512)[tid] = packed;
+  if (lse && tid == 0) lse[bq * 16 + h] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
 
 hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, const uint8_t* swa, int32_t S,
@@ -309,8 +316,8 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, const uint8_
                      part_ml, bq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq), dim3(kThreads), 0, stream, part_o, part_ml, splits, bq,
-                     out, lse);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq, 16), dim3(kThreads), 0, stream, part_o, part_ml, splits,
+                     bq, out, lse);
   return hipGetLastError();
 }
 

@@ -72,3 +72,25 @@ def integers(config_id: int, tag: str, shape, lo: int, hi: int) -> np.ndarray:
 def seq_rows(config_id: int, tag: str, b: int, t0: int, n: int, width: int, per_seq_rows: int) -> np.ndarray:
     """Rows t0..t0+n of sequence b, where sequence b owns rows [b*per_seq_rows, (b+1)*per_seq_rows)."""
     return normal_rows(config_id, tag, b * per_seq_rows + t0, n, width)
+
+
+def torch_normal_rows(config_id: int, tag: str, row0: int, n_rows: int, width: int, device="cuda"):
+    """Rows [row0, row0 + n_rows) of an endless N(0, 1) fp32 matrix drawn on the
+    device with torch's generator, seeded per 65,536-row chunk like normal_rows.
+    Same recipe, different stream of numbers: both sides of a comparison must use
+    the same function (the host side copies the device rows)."""
+    import torch
+    out = torch.empty((n_rows, width), dtype=torch.float32, device=device)
+    r = row0
+    while r < row0 + n_rows:
+        c = r // CHUNK_ROWS
+        c0 = c * CHUNK_ROWS
+        take_lo = r - c0
+        take_hi = min(CHUNK_ROWS, row0 + n_rows - c0)
+        seed = int(np.random.SeedSequence(BASE_SEED + int(config_id), spawn_key=(tag_id(tag), int(c))).generate_state(1)[0])
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        block = torch.randn((take_hi, width), generator=g, dtype=torch.float32, device=device)
+        out[r - row0:r - row0 + (take_hi - take_lo)] = block[take_lo:take_hi]
+        r = c0 + take_hi
+    return out
