@@ -75,6 +75,7 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * kPStride];
   __shared__ float s_m[16], s_l[16], s_alpha[16];
   __shared__ int s_valid[kAttnTile];
+  __shared__ int32_t s_ent[kTilesPerQuery * kAttnTile];
 
   const int split = blockIdx.x;
   const int64_t bq = blockIdx.y;
@@ -102,50 +103,73 @@ __global__ void __launch_bounds__(kThreads)
 
   const int t_begin = split * tps;
   const int t_end = min(kTilesPerQuery, t_begin + tps);
+  // this split's Top-K entries (main-KV slots only), staged once
+  for (int i = tid; i < tps * kAttnTile; i += kThreads) {
+    const int slot = t_begin * kAttnTile + i;
+    s_ent[i] = (slot < 512 && cap > 0) ? topk[bq * 512 + slot] : -1;
+  }
+  __syncthreads();
+
+  // thread -> (key j of the tile, 64-channel part)
+  const int j = tid & 31, part = tid >> 5;
+  // raw bytes of one tile for this thread: main rows use w[0..1] (32 code
+  // bytes) and sc (4 scale bytes); window rows use w[0..3] (64 E4M3 bytes).
+  // Loads are unconditional from a clamped address (masked later), so that a
+  // tile's loads and the next tile's prefetch all stay in flight together.
+  auto load_tile = [&](int tile, uint4* w, uint32_t& sc, bool& valid) {
+    const int slot = tile * kAttnTile + j;
+    if (tile * kAttnTile < 512) {  // uniform per tile: 512 is a multiple of the tile
+      const int32_t e = s_ent[(tile - t_begin) * kAttnTile + j];
+      valid = e >= 0;
+      if (cap > 0) {  // uniform; an empty cache has no row to stand in
+        const int64_t row = (int64_t)b * cap + (valid ? e : 0);
+        const uint4* cp = reinterpret_cast<const uint4*>(kv_codes + row * 256 + 32 * part);
+        w[0] = cp[0];
+        w[1] = cp[1];
+        sc = *reinterpret_cast<const uint32_t*>(kv_scales + row * 32 + 4 * part);
+      }
+    } else {
+      const int64_t pos = (int64_t)p - 127 + (slot - 512);
+      valid = pos >= 0;
+      const uint4* sp = reinterpret_cast<const uint4*>(swa + ((int64_t)b * S + (valid ? pos % S : 0)) * 512 + 64 * part);
+      w[0] = sp[0];
+      w[1] = sp[1];
+      w[2] = sp[2];
+      w[3] = sp[3];
+    }
+  };
+  uint4 wc[4] = {}, wn[4] = {};
+  uint32_t scc = 0, scn = 0;
+  bool vc = false, vn = false;
+  load_tile(t_begin, wc, scc, vc);
   for (int tile = t_begin; tile < t_end; tile++) {
-    // ---------------- gather + dequantise 32 keys
+    load_tile(min(tile + 1, t_end - 1), wn, scn, vn);  // prefetch (the last tile reloads itself)
+    // ---------------- dequantise this tile's 32 keys into LDS
     {
-      const int j = tid & 31, part = tid >> 5;  // key, 64-dim part
-      const int slot = tile * kAttnTile + j;
       float v[64];
-      bool valid = false;
-      if (slot < 512) {
-        const int32_t e = topk[bq * 512 + slot];
-        if (e >= 0) {
-          valid = true;
-          const int64_t row = (int64_t)b * cap + e;
-          const uint4* cp = reinterpret_cast<const uint4*>(kv_codes + row * 256 + 32 * part);
-          const uint4 c0 = cp[0], c1 = cp[1];
-          const uint32_t sc = *reinterpret_cast<const uint32_t*>(kv_scales + row * 32 + 4 * part);
-          const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      if (tile * kAttnTile < 512) {
+        const uint32_t cw[8] = {wc[0].x, wc[0].y, wc[0].z, wc[0].w, wc[1].x, wc[1].y, wc[1].z, wc[1].w};
 #pragma unroll
-          for (int g = 0; g < 4; g++) {
-            const float s = e4m3_decode((sc >> (8 * g)) & 0xFFu);
+        for (int g = 0; g < 4; g++) {
+          const float s = e4m3_decode((scc >> (8 * g)) & 0xFFu);
 #pragma unroll
-            for (int w = 0; w < 2; w++) {
-              const uint32_t word = cw[2 * g + w];
+          for (int w = 0; w < 2; w++) {
+            const uint32_t word = cw[2 * g + w];
 #pragma unroll
-              for (int n = 0; n < 8; n++) v[16 * g + 8 * w + n] = e2m1_decode((word >> (4 * n)) & 15u) * s;
-            }
+            for (int n = 0; n < 8; n++) v[16 * g + 8 * w + n] = e2m1_decode((word >> (4 * n)) & 15u) * s;
           }
         }
       } else {
-        const int64_t pos = (int64_t)p - 127 + (slot - 512);
-        if (pos >= 0) {
-          valid = true;
-          const uint4* sp = reinterpret_cast<const uint4*>(swa + ((int64_t)b * S + pos % S) * 512 + 64 * part);
 #pragma unroll
-          for (int w = 0; w < 4; w++) {
-            const uint4 x = sp[w];
-            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+        for (int w = 0; w < 4; w++) {
+          const uint32_t xw[4] = {wc[w].x, wc[w].y, wc[w].z, wc[w].w};
 #pragma unroll
-            for (int k = 0; k < 4; k++)
+          for (int k = 0; k < 4; k++)
 #pragma unroll
-              for (int n = 0; n < 4; n++) v[16 * w + 4 * k + n] = e4m3_decode((xw[k] >> (8 * n)) & 0xFFu);
-          }
+            for (int n = 0; n < 4; n++) v[16 * w + 4 * k + n] = e4m3_decode((xw[k] >> (8 * n)) & 0xFFu);
         }
       }
-      if (!valid) {
+      if (!vc) {
 #pragma unroll
         for (int c = 0; c < 64; c++) v[c] = 0.0f;
       }
@@ -157,7 +181,7 @@ __global__ void __launch_bounds__(kThreads)
       // fp16 [dim][key]
 #pragma unroll
       for (int c = 0; c < 64; c++) s_kt[(64 * part + c) * kKtStride + j] = (_Float16)v[c];
-      if (part == 0) s_valid[j] = valid;
+      if (part == 0) s_valid[j] = vc;
     }
     __syncthreads();
 
@@ -226,6 +250,12 @@ __global__ void __launch_bounds__(kThreads)
       }
     }
     __syncthreads();
+    wc[0] = wn[0];
+    wc[1] = wn[1];
+    wc[2] = wn[2];
+    wc[3] = wn[3];
+    scc = scn;
+    vc = vn;
   }
 
   // ---------------- epilogue: rows 4*(lane/16)+i are heads, column lane%16 a dim

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/csa2.h"
+#include "csa2.h"
 #include "kernels.hpp"
 
 namespace {
