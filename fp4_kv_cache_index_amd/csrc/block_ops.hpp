@@ -56,6 +56,21 @@ __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
+// Exclusive offsets of v[0..n) (LDS) into off[] (LDS); returns the total.
+__device__ __forceinline__ int block_offsets(const int* v, int* off, int n, int* tmp) {
+  int carry = 0;
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int c = base + threadIdx.x;
+    const int x = c < n ? v[c] : 0;
+    int tot;
+    const int ex = block_scan_excl(x, tmp, &tot);
+    if (c < n) off[c] = carry + ex;
+    carry += tot;
+  }
+  __syncthreads();
+  return carry;
+}
+
 struct SelShared {
   uint32_t red[16][8];
   uint64_t wmin[16], wmax[16];

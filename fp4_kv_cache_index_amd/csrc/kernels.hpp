@@ -29,14 +29,21 @@ constexpr int kPool = kPoolBlocks * kBlock;
 inline int64_t full_chunks(int32_t capacity) { return ((int64_t)capacity + kFullChunk - 1) / kFullChunk; }
 inline int64_t reindex_chunks() { return kPool / kReindexChunk; }
 
-// Workspace of one index call, per (sequence, query): sorted candidate lists
-// of each chunk (u64 keys), their counts, and the sorted block lists for the pool.
+// Workspace of one index call, per (sequence, query) and chunk: the chunk's
+// Top-512 u64 keys and their top-m summary, the chunk's block-maximum keys and
+// their summary (all unordered), and the counts.
 struct IndexWs {
   uint64_t* lists;    // [BQ][chunks][512]
+  uint64_t* summ;     // [BQ][chunks][512] (first min(count, m) used)
   uint32_t* counts;   // [BQ][chunks]
   uint64_t* blists;   // [BQ][chunks][chunk/8]
+  uint64_t* bsumm;    // [BQ][chunks][chunk/8]
   uint32_t* bcounts;  // [BQ][chunks]
 };
+// summary length for lists of `per_list` keys from which the top `k` overall
+// are selected over `n_lists` lists: the mean share plus four standard
+// deviations (rarely exceeded by i.i.d. scores), bounded by what one merge stages
+int summary_len(int k, int64_t n_lists, int per_list, int cap);
 size_t index_ws_bytes(int64_t bq, int32_t capacity);
 IndexWs index_ws_carve(void* ws, int64_t bq, int64_t chunks, int chunk);
 
