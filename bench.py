@@ -195,48 +195,74 @@ class Workload:
         return by
 
 
-def cpu_baseline(wl, steps=2):
-    """The oracle, as it stands, on the first sequences of the same workload."""
-    import oracle as orc
-    h = wl.host_rows
-    hs = h["kv"].shape[0]
-    r, B, Q = wl.r, wl.B, wl.Q
-    t0 = time.time()
-    oc = orc.Cache(hs, wl.cap, r)
-    orc.quantize_append(oc, h["kv"], h["ik"], logits=h["lg"])
-    swas = []
-    tok_before = wl.E_before * r
-    for l in range(wl.L):
-        s = np.zeros((hs, wl.S, 512), np.uint8)
-        orc.swa_append(s, wl.swa_rows[l][:hs].cpu().numpy(), np.full(hs, tok_before, np.int32))
-        swas.append(s)
-    inp = {k: (v[:hs].cpu().numpy() if isinstance(v, torch.Tensor) else
-               ([t[:hs].float().cpu().numpy() for t in v] if isinstance(v, list) else None))
-           for k, v in wl.inputs[0].items()}
-    q_pos = wl.q_pos[:hs].cpu().numpy() if wl.q_pos is not None else None
-    log(f"oracle sample set up in {time.time() - t0:.1f}s ({hs} sequences)")
-    times = []
-    for s_i in range(steps):
+class OracleStep:
+    """The oracle's copy of the first `hs` sequences of a workload: built from the
+    same seeded rows (copied from where they were drawn), advanced by the same
+    step inputs.  `qsel` restricts every layer to a subset of query slots."""
+
+    def __init__(self, wl, qsel=None):
+        import oracle as orc
+        self.orc, self.wl = orc, wl
+        h = wl.host_rows
+        self.hs = hs = h["kv"].shape[0]
+        r = wl.r
+        self.oc = orc.Cache(hs, wl.cap, r)
+        orc.quantize_append(self.oc, h["kv"], h["ik"], logits=h["lg"])
+        self.swas = []
+        tok_before = wl.E_before * r
+        for l in range(wl.L):
+            s = np.zeros((hs, wl.S, 512), np.uint8)
+            orc.swa_append(s, wl.swa_rows[l][:hs].cpu().numpy(), np.full(hs, tok_before, np.int32))
+            self.swas.append(s)
+        self.qsel = qsel
+        inp = wl.inputs[0]
+        pick = (lambda a: a[:, qsel]) if qsel is not None else (lambda a: a)
+        self.inp = dict(kv=inp["kv"][:hs].cpu().numpy(), ik=inp["ik"][:hs].cpu().numpy(),
+                        lg=inp["lg"][:hs].cpu().numpy() if inp["lg"] is not None else None,
+                        x=[t[:hs].cpu().numpy() for t in inp["x"]],
+                        iq=[pick(t[:hs].cpu().numpy()) for t in inp["iq"]],
+                        q=[pick(t[:hs].float().cpu().numpy()) for t in inp["q"]])
+        self.q_pos = pick(wl.q_pos[:hs].cpu().numpy()) if wl.q_pos is not None else None
+
+    def step(self, want_scores=False):
+        """One group step; returns per-layer dict(topk, pool, scores, out)."""
+        orc, wl, oc, inp = self.orc, self.wl, self.oc, self.inp
         if not wl.decode:
             oc.length[:] = wl.E_before
-        t = time.time()
         orc.quantize_append(oc, inp["kv"], inp["ik"], logits=inp["lg"])
-        seq = oc.length * r if wl.decode else np.full(hs, tok_before + wl.T_step, np.int32)
-        topk, pool = None, None
+        seq = (oc.length * wl.r).astype(np.int32) if wl.decode else \
+            np.full(self.hs, wl.E_before * wl.r + wl.T_step, np.int32)
+        res, topk, pool = [], None, None
         for l, mode in enumerate(wl.group):
-            orc.swa_append(swas[l], inp["x"][l], seq.astype(np.int32))
+            orc.swa_append(self.swas[l], inp["x"][l], seq)
+            scores = None
             if mode in ("full", "full_pool"):
-                topk, pool, _ = orc.index_topk(oc, orc.FULL, inp["iq"][l], q_pos=q_pos, want_pool=mode == "full_pool")
+                topk, pool, scores = orc.index_topk(oc, orc.FULL, inp["iq"][l], q_pos=self.q_pos,
+                                                    want_pool=mode == "full_pool", want_scores=want_scores)
             elif mode == "reindex":
-                topk, _, _ = orc.index_topk(oc, orc.REINDEX, inp["iq"][l], q_pos=q_pos, pool_in=pool)
-            orc.attend(oc, topk, swas[l], inp["q"][l], SM_SCALE, q_pos=q_pos)
+                topk, _, scores = orc.index_topk(oc, orc.REINDEX, inp["iq"][l], q_pos=self.q_pos, pool_in=pool,
+                                                 want_scores=want_scores)
+            out, lse = orc.attend(oc, topk, self.swas[l], inp["q"][l], SM_SCALE, q_pos=self.q_pos)
+            res.append(dict(topk=topk, pool=pool if mode == "full_pool" else None, scores=scores, out=out, lse=lse))
+        return res
+
+
+def cpu_baseline(wl, steps=2):
+    """The oracle, as it stands, on the first sequences of the same workload."""
+    t0 = time.time()
+    ost = OracleStep(wl)
+    log(f"oracle sample set up in {time.time() - t0:.1f}s ({ost.hs} sequences)")
+    times = []
+    for s_i in range(steps):
+        t = time.time()
+        ost.step()
         times.append(time.time() - t)
         log(f"oracle step {s_i}: {times[-1]:.2f}s")
     t_step = float(np.median(times))
-    value = wl.L / t_step * hs / B
-    return dict(value=value, unit=UNIT, cores=int(min(orc.num_threads(), hs * Q)), kind="oracle",
-                sample=f"{steps} group steps of the first {hs} of {B} sequences (full context, all {wl.L} layers), "
-                       f"median {t_step:.2f}s per step, scaled by {B}/{hs} to the whole batch")
+    value = wl.L / t_step * ost.hs / wl.B
+    return dict(value=value, unit=UNIT, cores=int(min(ost.orc.num_threads(), ost.hs * wl.Q)), kind="oracle",
+                sample=f"{steps} group steps of the first {ost.hs} of {wl.B} sequences (full context, all {wl.L} "
+                       f"layers), median {t_step:.2f}s per step, scaled by {wl.B}/{ost.hs} to the whole batch")
 
 
 def traffic_from_profiles(wl, kernel_name):
