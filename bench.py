@@ -265,6 +265,64 @@ def cpu_baseline(wl, steps=2):
                        f"layers), median {t_step:.2f}s per step, scaled by {wl.B}/{ost.hs} to the whole batch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters to bytes (run under the same counter pass)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize_counters(fetch_csv, write_csv, workload_name):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of `bench.py --copy-calibration` into HBM bytes per Full indexer call."""
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        acc, copies = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, grid = r["Kernel_Name"], int(r["Grid_Size"])
+            acc.setdefault((name, grid), []).append(float(r["Counter_Value"]))
+            if "copyBuffer" in name:
+                copies.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        # the calibration copies are the last three device copies of the run
+        return acc, [v for _, v in sorted(copies)[-3:]]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        acc, copy = per_kernel(path, counter)
+        scan = [v for (n, g), vals in acc.items() if "index_scan_kernel<4096, false>" in n for v in vals]
+        # the Full call's merge has twice the workgroups of the Reindex merge
+        merge_grids = [g for (n, g) in acc if "index_merge_kernel" in n]
+        merge = [v for (n, g), vals in acc.items() if "index_merge_kernel" in n and merge_grids and
+                 g == max(merge_grids) for v in vals]
+        kib_copy = float(np.median(copy)) if copy else float("nan")
+        factor = COPY_BYTES / (kib_copy * 1024.0)
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_kib_scan"] = float(np.mean(scan)) if scan else None
+        out[f"{key}_kib_merge"] = float(np.mean(merge)) if merge else None
+        out[f"{key}_kib_copy_{COPY_BYTES >> 20}MiB"] = kib_copy
+        out[f"{key}_factor"] = factor
+    tot = 0.0
+    for key in ("fetch", "write"):
+        tot += ((out[f"{key}_kib_scan"] or 0.0) + (out[f"{key}_kib_merge"] or 0.0)) * 1024.0 * out[f"{key}_factor"]
+    src = "index.hip"
+    sha = hashlib.sha256(open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", src), "rb").read()).hexdigest()
+    out.update(source=src, source_sha256=sha, workload=workload_name, hbm_bytes_per_launch=round(tot))
+    path = os.path.join(ROOT, "profiles", f"counters_index_full_{workload_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def traffic_from_profiles(wl, kernel_name):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter
     summaries, if they were taken on the kernel source as it is now."""
@@ -290,7 +348,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: all)")
     ap.add_argument("--roofline-iters", type=int, default=30)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters_index_full_<workload>.json from two rocprofv3 --pmc CSVs")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, synth.WORKLOADS[args.config]["name"])
+        return
     if args.gpus != 1:
         print(f"bench.py: this build targets one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is described, not built)", file=sys.stderr)
@@ -373,6 +438,8 @@ def main():
                 bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
     log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
 
+    if args.copy_calibration:
+        copy_calibration()
     cpu = None
     if want_cpu:
         cpu = cpu_baseline(wl)
