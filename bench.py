@@ -162,7 +162,6 @@ class Workload:
         seq = c.length if (self.decode and self.r == 1) else self.seq_after
         topk = None
         for l, mode in enumerate(self.group):
-            csa.swa_append(swas[l], inp["x"][l], seq)
             if mode in ("full", "full_pool"):
                 csa.index_score_topk(c, csa.FULL, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
                                      pool_out=self.pool if mode == "full_pool" else None, ws=self.ws_idx)
@@ -171,8 +170,9 @@ class Workload:
                 csa.index_score_topk(c, csa.REINDEX, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
                                      pool_in=self.pool, ws=self.ws_idx)
                 topk = self.topk[l]
+            # the layer's window append runs inside its attention launch
             csa.sparse_attend(c, topk, swas[l], inp["q"][l], self.out[l], SM_SCALE, q_pos=self.q_pos,
-                              ws=self.ws_att)
+                              ws=self.ws_att, swa_x=inp["x"][l], swa_len=seq)
 
     def full_index(self, i):
         csa = self.csa

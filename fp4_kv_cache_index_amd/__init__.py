@@ -70,7 +70,8 @@ def lib():
         L.csa2_index_score_topk.restype = ctypes.c_int
         L.csa2_index_score_topk.argtypes = [cp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.csa2_sparse_attend.restype = ctypes.c_int
-        L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz, vp]
+        L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz,
+                                            vp]
         L.csa2_workspace_bytes.restype = sz
         L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32]
         L.csa2_status_string.restype = ctypes.c_char_p
@@ -188,7 +189,11 @@ def index_score_topk(cache: Cache, mode, iq, topk_out, iw=None, q_pos=None, pool
     _check(rc, "csa2_index_score_topk")
 
 
-def sparse_attend(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=None, ws=None, stream=None):
+def sparse_attend(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=None, ws=None, stream=None,
+                  swa_x=None, swa_len=None):
+    """Attention of one layer; with `swa_x` ([B][T][512] f32) and `swa_len` ([B]
+    i32 tokens after the append) the layer's new window tokens are appended to
+    `swa` in the same launch first."""
     B, Q = q.shape[0], q.shape[1]
     S = swa.shape[1]
     _expect(q, torch.bfloat16, (cache.batch, Q, HEADS, D), "q")
@@ -199,11 +204,16 @@ def sparse_attend(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=Non
         _expect(lse, torch.float32, (cache.batch, Q, HEADS), "lse")
     if q_pos is not None:
         _expect(q_pos, torch.int32, (cache.batch, Q), "q_pos")
+    T = 0
+    if swa_x is not None:
+        T = swa_x.shape[1]
+        _expect(swa_x, torch.float32, (cache.batch, T, D), "swa_x")
+        _expect(swa_len, torch.int32, (cache.batch,), "swa_len")
     need = workspace_bytes(OP_ATTEND, cache.batch, Q, cache.capacity)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
     st = cache.struct()
-    rc = lib().csa2_sparse_attend(ctypes.byref(st), _ptr(topk), _ptr(swa), S, _ptr(q), _ptr(q_pos),
-                                  float(sm_scale), _ptr(out), _ptr(lse), Q, _ptr(ws),
+    rc = lib().csa2_sparse_attend(ctypes.byref(st), _ptr(topk), _ptr(swa), S, _ptr(swa_x), _ptr(swa_len), T,
+                                  _ptr(q), _ptr(q_pos), float(sm_scale), _ptr(out), _ptr(lse), Q, _ptr(ws),
                                   ws.numel() if ws is not None else 0, _stream(stream))
     _check(rc, "csa2_sparse_attend")

@@ -3,18 +3,30 @@
 // 128-token FP8 sliding window, one softmax over both, key = value (the report
 // stores one 512-channel latent per entry; ai.info "Main Findings";
 // technologiesdigest "CSA2": every layer keeps its own query and window KV).
+// Optionally the same launch first appends the layer's new window tokens.
 //
 // Key slots per query: 0..511 = the Top-512 list, 512..639 = window positions
 // p-127..p.  A workgroup (4 waves) walks a range of slots in tiles of 32:
-//   gather + dequantise: E2M1 code * E4M3 scale (and plain E4M3 for the window)
-//     is exact in both bf16 and fp16, so the tile lands in LDS twice: bf16
-//     [key][dim] for Q.K^T and fp16 [dim][key] for P.V;
-//   S = Q K^T on v_mfma_f32_16x16x32_bf16 (16 heads = the 16 MFMA rows; wave w
-//     covers dims 128w..128w+127 and the four partial S are summed in LDS);
+//   gather: thread (kg, grp) owns keys 4kg..4kg+3 of the tile and channels
+//     16grp..16grp+15, i.e. one E4M3 scale group per key (8 code bytes + 1
+//     scale byte, or 16 window bytes);
+//   dequantise: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the E2M1 values
+//     exactly and one v_pk_mul_f16 by the group scale gives x = code * scale,
+//     exact in fp16 (at most 6 significant bits, |x| in [2^-10, 2688]); window
+//     bytes widen exactly with v_cvt_scalef32_pk_f16_fp8.  The tile lands in
+//     LDS as fp16 [key][dim] for Q.K^T and fp16 [dim][key] for P.V;
+//   S = Q K^T on v_mfma_f32_16x16x32_f16: the bf16 query is scaled per head by
+//     a power of two that puts its largest element in [2^14, 2^15), which makes
+//     the fp16 copy exact for every element within 2^-28 of the head's largest,
+//     and the scores are scaled back exactly (16 heads = the 16 MFMA rows; wave
+//     w covers dims 128w..128w+127 and the four partial S are summed in LDS);
 //   online softmax in fp32 (running max and sum per head);
 //   O += P V on v_mfma_f32_16x16x32_f16, wave w owning output dims 128w.. .
 // With several splits per query the unnormalised partials (O, max, sum) go to
-// the workspace and a merge kernel combines them by log-sum-exp weights.
+// the workspace and a second kernel merges them by log-sum-exp weights, one
+// workgroup per (query, head).  (Merging in the last workgroup of each query
+// needs a device-scope release per workgroup, an L2 write-back that costs more
+// on gfx950 than the second launch.)
 #include <hip/hip_runtime.h>
 
 #include "codec.hpp"
@@ -23,37 +35,55 @@
 namespace csa2 {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kKbStride = 520;  // bf16 elements per key row (512 + pad)
-constexpr int kKtStride = 40;   // fp16 elements per dim row (32 keys + pad)
+constexpr int kKStride = 520;  // fp16 per key row of the [key][dim] tile (512 + pad)
+constexpr int kVStride = 40;   // fp16 per dim row of the [dim][key] tile (32 keys + pad)
 constexpr int kPStride = 40;
 constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
+constexpr int kMaxSplits = 10;
 
 int attend_splits(int64_t bq) {
   int64_t s = (256 + bq - 1) / bq;
   if (s < 1) s = 1;
-  if (s > 10) s = 10;
+  if (s > kMaxSplits) s = kMaxSplits;
   const int tps = (int)((kTilesPerQuery + s - 1) / s);
   return (kTilesPerQuery + tps - 1) / tps;
 }
 
 static inline int tiles_per_split(int splits) { return (kTilesPerQuery + splits - 1) / splits; }
 
+// [partial O: splits x bq x 16 x 512 f32][partial (max, sum): splits x bq x 16 x 2 f32]
 size_t attend_ws_bytes(int64_t bq) {
   const int s = attend_splits(bq);
   if (s == 1) return 0;
-  return (size_t)s * bq * (16 * 512 * 4 + 16 * 2 * 4) + 256;
+  return 256 + (size_t)s * bq * (16 * 512 * 4 + 16 * 2 * 4);
 }
 
-__device__ __forceinline__ int32_t attn_query_pos(const int32_t* q_pos, const int32_t* length, int32_t ratio, int b,
-                                                  int q, int Q) {
-  return q_pos ? q_pos[(int64_t)b * Q + q] : length[b] * ratio - Q + q;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_exact(float v) { return (uint16_t)(__float_as_uint(v) >> 16); }
+struct AttnArgs {
+  const uint8_t* kv_codes;
+  const uint8_t* kv_scales;
+  const int32_t* length;
+  int32_t cap, ratio;
+  const int32_t* topk;
+  uint8_t* swa;
+  int32_t S;
+  const float* swa_x;      // [B][swa_T][512] new window tokens, or null
+  const int32_t* swa_len;  // [B] tokens after the append
+  int32_t swa_T;
+  const uint16_t* q;
+  const int32_t* q_pos;
+  float sm_scale;
+  int32_t Q;
+  int32_t tps, splits;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  int64_t bq_total;
+};
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
@@ -61,127 +91,200 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)(u >> 16);
 }
 
-__global__ void __launch_bounds__(kThreads)
-    attend_kernel(const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales,
-                  const int32_t* __restrict__ length, int32_t cap, int32_t ratio, const int32_t* __restrict__ topk,
-                  const uint8_t* __restrict__ swa, int32_t S, const uint16_t* __restrict__ q,
-                  const int32_t* __restrict__ q_pos, float sm_scale, int32_t Q, int tps,
-                  uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-                  float* __restrict__ part_ml, int64_t bq_total) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_kb[kAttnTile * kKbStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_kt[512 * kKtStride];
+__device__ __forceinline__ uint32_t h2_bits(v2h h) { return __builtin_bit_cast(uint32_t, h); }
+
+// 8 E2M1 codes (low nibble first) times a group scale, as four fp16x2 words
+__device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
+  o[0] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
+  o[1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
+  o[2] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
+  o[3] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
+}
+
+// 16 window channels of a new token: fp32 -> E4M3 bytes, as the window append stores them
+__device__ __forceinline__ uint4 encode16(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const float4 v = *reinterpret_cast<const float4*>(x + 4 * k);
+    w[k] = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) | (e4m3_encode(v.w) << 24);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[kAttnTile * kKStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[512 * kVStride];
   __shared__ float s_red[4][2][256];
   __shared__ float s_sfull[16][kAttnTile];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * kPStride];
   __shared__ float s_m[16], s_l[16], s_alpha[16];
+  __shared__ float s_qmax[4][16];
+  __shared__ float s_qfac[16];
   __shared__ int s_valid[kAttnTile];
-  __shared__ int32_t s_ent[kTilesPerQuery * kAttnTile];
 
   const int split = blockIdx.x;
   const int64_t bq = blockIdx.y;
+  const int Q = a.Q;
   const int b = (int)(bq / Q), qi = (int)(bq % Q);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t p = attn_query_pos(q_pos, length, ratio, b, qi, Q);
+  const int32_t p = a.q_pos ? a.q_pos[bq] : a.length[b] * a.ratio - Q + qi;
+  // new window tokens are positions new_lo .. new_hi-1
+  const int32_t new_hi = a.swa_x ? a.swa_len[b] : 0;
+  const int32_t new_lo = a.swa_x ? new_hi - a.swa_T : 0;
 
-  // Q operand of Q.K^T: lane l holds head l%16, dims 128*wave + 32*kk + 8*(l/16) .. +7
-  v8bf qa[4];
+  const int t_begin = split * a.tps;
+  const int t_end = min(kTilesPerQuery, t_begin + a.tps);
+  const int kg = tid & 7, grp = tid >> 3;  // keys 4kg..4kg+3, channels 16grp..16grp+15
+  const int32_t* tk = a.topk + bq * 512 + 4 * kg;
+
+  // Raw bytes of a tile for this thread: main rows use w[i].x/.y (16 codes) and
+  // w[i].z (the scale byte); window rows use all 16 bytes.  Main-row loads are
+  // unconditional from a clamped row (masked through the scale) so that a tile's
+  // loads and the next tile's all stay in flight together.
+  auto load_idx = [&](int tile) -> int4 {
+    if (tile < t_end && tile * kAttnTile < 512) return *reinterpret_cast<const int4*>(tk + tile * kAttnTile);
+    return make_int4(-1, -1, -1, -1);
+  };
+  auto load_tile = [&](int tile, int4 e4, uint4* w, uint32_t& vmask) {
+    vmask = 0;
+    if (tile * kAttnTile < 512) {  // uniform per tile: 512 is a multiple of the tile
+      if (a.cap > 0) {             // uniform; an empty cache has no row to stand in
+        const int32_t es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const bool valid = es[i] >= 0;
+          vmask |= (uint32_t)valid << i;
+          const int64_t row = (int64_t)b * a.cap + (valid ? es[i] : 0);
+          const uint2 c = *reinterpret_cast<const uint2*>(a.kv_codes + row * 256 + 8 * grp);
+          w[i] = make_uint4(c.x, c.y, a.kv_scales[row * 32 + grp], 0u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);
+        const bool valid = pos >= 0;
+        vmask |= (uint32_t)valid << i;
+        if (pos >= new_lo && pos < new_hi) {
+          w[i] = encode16(a.swa_x + ((int64_t)b * a.swa_T + (pos - new_lo)) * 512 + 16 * grp);
+        } else {
+          w[i] = *reinterpret_cast<const uint4*>(a.swa + ((int64_t)b * a.S + (valid ? pos % a.S : 0)) * 512 + 16 * grp);
+        }
+      }
+    }
+  };
+
+  uint4 wc[4] = {}, wn[4] = {};
+  uint32_t vc = 0, vn = 0;
+  int4 ec = load_idx(t_begin);
+  int4 en = load_idx(t_begin + 1);
+
+  // ---------------- fused window append: this workgroup's share of the new tokens
+  if (a.swa_x) {
+    const int rank = qi * a.splits + split, n_w = Q * a.splits;
+    for (int t = rank; t < a.swa_T; t += n_w) {
+      const int32_t pos = new_lo + t;
+      const float2 v = *reinterpret_cast<const float2*>(a.swa_x + ((int64_t)b * a.swa_T + t) * 512 + 2 * tid);
+      const uint32_t c = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8);
+      *reinterpret_cast<uint16_t*>(a.swa + ((int64_t)b * a.S + pos % a.S) * 512 + 2 * tid) = (uint16_t)c;
+    }
+  }
+
+  // ---------------- query: lane holds head lane%16, dims 128*wave + 32*kk + 8*(lane/16) .. +7
+  v8h qa[4];
   {
-    const uint16_t* qrow = q + (bq * 16 + (lane & 15)) * 512 + 128 * wave + 8 * (lane >> 4);
+    const uint16_t* qrow = a.q + (bq * 16 + (lane & 15)) * 512 + 128 * wave + 8 * (lane >> 4);
+    uint4 qraw[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) qraw[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+    load_tile(t_begin, ec, wc, vc);  // the first tile's rows load while the query is scaled
+    float qf[4][8];
+    float amax = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-      qa[kk] = __builtin_bit_cast(v8bf, x);
+      const uint32_t xw[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        qf[kk][2 * n] = __uint_as_float(xw[n] << 16);
+        qf[kk][2 * n + 1] = __uint_as_float(xw[n] & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * n]), fabsf(qf[kk][2 * n + 1])));
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (lane < 16) s_qmax[wave][lane] = amax;
+    if (tid < 16) {
+      s_m[tid] = -INFINITY;
+      s_l[tid] = 0.0f;
+    }
+    __syncthreads();
+    const int h = lane & 15;
+    const float hmax = fmaxf(fmaxf(s_qmax[0][h], s_qmax[1][h]), fmaxf(s_qmax[2][h], s_qmax[3][h]));
+    int ex;
+    frexpf(hmax, &ex);  // hmax = f * 2^ex, f in [0.5, 1); ex = 0 for a zero head
+    const int sh = min(127, max(-126, 15 - ex));
+    const float up = ldexpf(1.0f, sh);
+    if (tid < 16) s_qfac[tid] = ldexpf(a.sm_scale, -sh);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+#pragma unroll
+      for (int n = 0; n < 8; n++) qa[kk][n] = (_Float16)(qf[kk][n] * up);
     }
   }
   v4f acc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ct++) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-  if (tid < 16) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.0f;
-  }
 
-  const int t_begin = split * tps;
-  const int t_end = min(kTilesPerQuery, t_begin + tps);
-  // this split's Top-K entries (main-KV slots only), staged once
-  for (int i = tid; i < tps * kAttnTile; i += kThreads) {
-    const int slot = t_begin * kAttnTile + i;
-    s_ent[i] = (slot < 512 && cap > 0) ? topk[bq * 512 + slot] : -1;
-  }
-  __syncthreads();
-
-  // thread -> (key j of the tile, 64-channel part)
-  const int j = tid & 31, part = tid >> 5;
-  // raw bytes of one tile for this thread: main rows use w[0..1] (32 code
-  // bytes) and sc (4 scale bytes); window rows use w[0..3] (64 E4M3 bytes).
-  // Loads are unconditional from a clamped address (masked later), so that a
-  // tile's loads and the next tile's prefetch all stay in flight together.
-  auto load_tile = [&](int tile, uint4* w, uint32_t& sc, bool& valid) {
-    const int slot = tile * kAttnTile + j;
-    if (tile * kAttnTile < 512) {  // uniform per tile: 512 is a multiple of the tile
-      const int32_t e = s_ent[(tile - t_begin) * kAttnTile + j];
-      valid = e >= 0;
-      if (cap > 0) {  // uniform; an empty cache has no row to stand in
-        const int64_t row = (int64_t)b * cap + (valid ? e : 0);
-        const uint4* cp = reinterpret_cast<const uint4*>(kv_codes + row * 256 + 32 * part);
-        w[0] = cp[0];
-        w[1] = cp[1];
-        sc = *reinterpret_cast<const uint32_t*>(kv_scales + row * 32 + 4 * part);
-      }
-    } else {
-      const int64_t pos = (int64_t)p - 127 + (slot - 512);
-      valid = pos >= 0;
-      const uint4* sp = reinterpret_cast<const uint4*>(swa + ((int64_t)b * S + (valid ? pos % S : 0)) * 512 + 64 * part);
-      w[0] = sp[0];
-      w[1] = sp[1];
-      w[2] = sp[2];
-      w[3] = sp[3];
-    }
-  };
-  uint4 wc[4] = {}, wn[4] = {};
-  uint32_t scc = 0, scn = 0;
-  bool vc = false, vn = false;
-  load_tile(t_begin, wc, scc, vc);
   for (int tile = t_begin; tile < t_end; tile++) {
-    load_tile(min(tile + 1, t_end - 1), wn, scn, vn);  // prefetch (the last tile reloads itself)
-    // ---------------- dequantise this tile's 32 keys into LDS
+    // prefetch the next tile's rows and the indices of the one after
+    const int4 e2 = load_idx(tile + 2);
+    if (tile + 1 < t_end) load_tile(tile + 1, en, wn, vn);
+    // ---------------- dequantise this tile's keys into LDS (fp16, both layouts)
     {
-      float v[64];
+      uint32_t hv[4][8];  // key i: channel pairs (2m, 2m+1) of the group, as fp16x2
       if (tile * kAttnTile < 512) {
-        const uint32_t cw[8] = {wc[0].x, wc[0].y, wc[0].z, wc[0].w, wc[1].x, wc[1].y, wc[1].z, wc[1].w};
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const float s = e4m3_decode((scc >> (8 * g)) & 0xFFu);
-#pragma unroll
-          for (int w = 0; w < 2; w++) {
-            const uint32_t word = cw[2 * g + w];
-#pragma unroll
-            for (int n = 0; n < 8; n++) v[16 * g + 8 * w + n] = e2m1_decode((word >> (4 * n)) & 15u) * s;
-          }
+        for (int i = 0; i < 4; i++) {
+          const uint32_t sc = ((vc >> i) & 1u) ? (wc[i].z & 0xFFu) : 0u;
+          const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc * 0x0101u, 1.0f, false);
+          fp4_group(wc[i].x, s2, hv[i]);
+          fp4_group(wc[i].y, s2, hv[i] + 4);
         }
       } else {
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-          const uint32_t xw[4] = {wc[w].x, wc[w].y, wc[w].z, wc[w].w};
+        for (int i = 0; i < 4; i++) {
+          const bool valid = (vc >> i) & 1u;
+          const uint32_t xw[4] = {valid ? wc[i].x : 0u, valid ? wc[i].y : 0u, valid ? wc[i].z : 0u,
+                                  valid ? wc[i].w : 0u};
 #pragma unroll
-          for (int k = 0; k < 4; k++)
-#pragma unroll
-            for (int n = 0; n < 4; n++) v[16 * w + 4 * k + n] = e4m3_decode((xw[k] >> (8 * n)) & 0xFFu);
+          for (int k = 0; k < 4; k++) {
+            hv[i][2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
+            hv[i][2 * k + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, true));
+          }
         }
       }
-      if (!vc) {
+      // [key][dim]: key 4kg+i, channels 16grp .. +15
 #pragma unroll
-        for (int c = 0; c < 64; c++) v[c] = 0.0f;
+      for (int i = 0; i < 4; i++) {
+        uint4* dst = reinterpret_cast<uint4*>(s_k + (4 * kg + i) * kKStride + 16 * grp);
+        dst[0] = make_uint4(hv[i][0], hv[i][1], hv[i][2], hv[i][3]);
+        dst[1] = make_uint4(hv[i][4], hv[i][5], hv[i][6], hv[i][7]);
       }
-      // bf16 [key][dim]
-      uint32_t* kb = reinterpret_cast<uint32_t*>(s_kb + j * kKbStride + 64 * part);
+      // [dim][key]: channel 16grp+c, keys 4kg .. 4kg+3
 #pragma unroll
-      for (int c = 0; c < 32; c++)
-        kb[c] = (uint32_t)f32_to_bf16_exact(v[2 * c]) | ((uint32_t)f32_to_bf16_exact(v[2 * c + 1]) << 16);
-      // fp16 [dim][key]
+      for (int m = 0; m < 8; m++) {
+        const uint32_t lo01 = (hv[0][m] & 0xFFFFu) | (hv[1][m] << 16);
+        const uint32_t lo23 = (hv[2][m] & 0xFFFFu) | (hv[3][m] << 16);
+        const uint32_t hi01 = (hv[0][m] >> 16) | (hv[1][m] & 0xFFFF0000u);
+        const uint32_t hi23 = (hv[2][m] >> 16) | (hv[3][m] & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(s_vt + (16 * grp + 2 * m) * kVStride + 4 * kg) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(s_vt + (16 * grp + 2 * m + 1) * kVStride + 4 * kg) = make_uint2(hi01, hi23);
+      }
+    }
+    if (grp == 0) {
 #pragma unroll
-      for (int c = 0; c < 64; c++) s_kt[(64 * part + c) * kKtStride + j] = (_Float16)v[c];
-      if (part == 0) s_valid[j] = vc;
+      for (int i = 0; i < 4; i++) s_valid[4 * kg + i] = (vc >> i) & 1u;
     }
     __syncthreads();
 
@@ -189,11 +292,11 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int th = 0; th < 2; th++) {
       v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = s_kb + (16 * th + (lane & 15)) * kKbStride + 128 * wave + 8 * (lane >> 4);
+      const _Float16* krow = s_k + (16 * th + (lane & 15)) * kKStride + 128 * wave + 8 * (lane >> 4);
 #pragma unroll
       for (int kk = 0; kk < 4; kk++) {
         const uint4 x = *reinterpret_cast<const uint4*>(krow + 32 * kk);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(v8bf, x), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], __builtin_bit_cast(v8h, x), sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; i++) s_red[wave][th][i * 64 + lane] = sacc[i];
@@ -205,7 +308,8 @@ __global__ void __launch_bounds__(kThreads)
       const float sv = s_red[0][th][i * 64 + l] + s_red[1][th][i * 64 + l] + s_red[2][th][i * 64 + l] +
                        s_red[3][th][i * 64 + l];
       const int head = 4 * (l >> 4) + i, key = 16 * th + (l & 15);
-      s_sfull[head][key] = s_valid[key] ? sv * sm_scale : -INFINITY;
+      // the head's factor undoes its query scale exactly and applies sm_scale
+      s_sfull[head][key] = s_valid[key] ? sv * s_qfac[head] : -INFINITY;
     }
     __syncthreads();
     // ---------------- online softmax: 16 threads per head, 2 keys each
@@ -245,21 +349,19 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int i = 0; i < 4; i++) acc[ct][i] *= al[i];
         const int dim = 128 * wave + 16 * ct + (lane & 15);
-        const uint4 kx = *reinterpret_cast<const uint4*>(s_kt + dim * kKtStride + 8 * (lane >> 4));
+        const uint4 kx = *reinterpret_cast<const uint4*>(s_vt + dim * kVStride + 8 * (lane >> 4));
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, __builtin_bit_cast(v8h, kx), acc[ct], 0, 0, 0);
       }
     }
     __syncthreads();
-    wc[0] = wn[0];
-    wc[1] = wn[1];
-    wc[2] = wn[2];
-    wc[3] = wn[3];
-    scc = scn;
+#pragma unroll
+    for (int i = 0; i < 4; i++) wc[i] = wn[i];
     vc = vn;
+    en = e2;
   }
 
   // ---------------- epilogue: rows 4*(lane/16)+i are heads, column lane%16 a dim
-  if (part_o == nullptr) {
+  if (a.splits == 1) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int h = 4 * (lane >> 4) + i;
@@ -268,12 +370,14 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int ct = 0; ct < 8; ct++) {
         const int dim = 128 * wave + 16 * ct + (lane & 15);
-        out[(bq * 16 + h) * 512 + dim] = f32_to_bf16_rne(acc[ct][i] * inv);
+        a.out[(bq * 16 + h) * 512 + dim] = f32_to_bf16_rne(acc[ct][i] * inv);
       }
     }
-    if (lse && tid < 16) lse[bq * 16 + tid] = s_l[tid] > 0.0f ? s_m[tid] + __logf(s_l[tid]) : -INFINITY;
-  } else {
-    float* po = part_o + ((int64_t)split * bq_total + bq) * 16 * 512;
+    if (a.lse && tid < 16) a.lse[bq * 16 + tid] = s_l[tid] > 0.0f ? s_m[tid] + __logf(s_l[tid]) : -INFINITY;
+    return;
+  }
+  {
+    float* po = a.part_o + ((int64_t)split * a.bq_total + bq) * 16 * 512;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int h = 4 * (lane >> 4) + i;
@@ -281,7 +385,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int ct = 0; ct < 8; ct++) po[h * 512 + 128 * wave + 16 * ct + (lane & 15)] = acc[ct][i];
     }
     if (tid < 16) {
-      float* pm = part_ml + ((int64_t)split * bq_total + bq) * 32;
+      float* pm = a.part_ml + ((int64_t)split * a.bq_total + bq) * 32;
       pm[2 * tid] = s_m[tid];
       pm[2 * tid + 1] = s_l[tid];
     }
@@ -293,61 +397,76 @@ __global__ void __launch_bounds__(kThreads)
 __global__ void __launch_bounds__(kThreads)
     attend_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
                         int64_t bq_total, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float s_m[16], s_l[16];
   const int64_t bq = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  if (tid < splits) {
-    const float* pm = part_ml + ((int64_t)tid * bq_total + bq) * 32 + 2 * h;
-    s_m[tid] = pm[0];
-    s_l[tid] = pm[1];
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < splits; s++) M = fmaxf(M, s_m[s]);
-  float L = 0.0f;
-  float w[10];
+  // every load is issued from a clamped split so they all stay in flight together
+  float ms[kMaxSplits], ls[kMaxSplits];
+  float2 v[kMaxSplits];
 #pragma unroll
-  for (int s = 0; s < 10; s++) {
-    w[s] = (s < splits && s_m[s] != -INFINITY) ? __expf(s_m[s] - M) : 0.0f;
-    L += s < splits ? w[s] * s_l[s] : 0.0f;
+  for (int s = 0; s < kMaxSplits; s++) {
+    const int sc = min(s, splits - 1);
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((int64_t)sc * bq_total + bq) * 32 + 2 * h);
+    ms[s] = ml.x;
+    ls[s] = ml.y;
+    v[s] = *reinterpret_cast<const float2*>(part_o + (((int64_t)sc * bq_total + bq) * 16 + h) * 512 + 2 * tid);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++)
+    if (s < splits) M = fmaxf(M, ms[s]);
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; s++) {
+    const float w = (s < splits && ms[s] != -INFINITY) ? __expf(ms[s] - M) : 0.0f;
+    L += w * ls[s];
+    o0 += w * v[s].x;
+    o1 += w * v[s].y;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-  for (int s = 0; s < 10; s++) {
-    if (s < splits) {
-      const float2 v = *reinterpret_cast<const float2*>(part_o + (((int64_t)s * bq_total + bq) * 16 + h) * 512 + 2 * tid);
-      o0 += w[s] * v.x;
-      o1 += w[s] * v.y;
-    }
-  }
   const uint32_t packed = (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16);
   reinterpret_cast<uint32_t*>(out + (bq * 16 + h) * 512)[tid] = packed;
   if (lse && tid == 0) lse[bq * 16 + h] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
 
-hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, const uint8_t* swa, int32_t S,
-                         const uint16_t* q, const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse,
-                         int32_t Q, void* ws, hipStream_t stream) {
+hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
+                         const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos,
+                         float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws, hipStream_t stream) {
   const int64_t bq = (int64_t)c.batch * Q;
   if (bq == 0) return hipSuccess;
-  const int splits = attend_splits(bq);
-  const int tps = tiles_per_split(splits);
-  float* part_o = nullptr;
-  float* part_ml = nullptr;
-  if (splits > 1) {
+  AttnArgs a;
+  a.kv_codes = c.kv_codes;
+  a.kv_scales = c.kv_scales;
+  a.length = c.length;
+  a.cap = c.capacity;
+  a.ratio = c.ratio;
+  a.topk = topk;
+  a.swa = swa;
+  a.S = S;
+  a.swa_x = swa_x;
+  a.swa_len = swa_len;
+  a.swa_T = swa_x ? swa_T : 0;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.sm_scale = sm_scale;
+  a.Q = Q;
+  a.splits = attend_splits(bq);
+  a.tps = tiles_per_split(a.splits);
+  a.out = out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.bq_total = bq;
+  if (a.splits > 1) {
     uint8_t* base = (uint8_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-    part_o = (float*)base;
-    part_ml = part_o + (int64_t)splits * bq * 16 * 512;
+    a.part_o = (float*)base;
+    a.part_ml = a.part_o + (int64_t)a.splits * bq * 16 * 512;
   }
-  hipLaunchKernelGGL(attend_kernel, dim3(splits, (unsigned)bq), dim3(kThreads), 0, stream, c.kv_codes, c.kv_scales,
-                     c.length, c.capacity, c.ratio, topk, swa, S, q, q_pos, sm_scale, Q, tps, out, lse, part_o,
-                     part_ml, bq);
+  hipLaunchKernelGGL(attend_kernel, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq, 16), dim3(kThreads), 0, stream, part_o, part_ml, splits,
-                     bq, out, lse);
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq, 16), dim3(kThreads), 0, stream, a.part_o, a.part_ml,
+                     a.splits, bq, out, lse);
   return hipGetLastError();
 }
 

@@ -93,20 +93,26 @@ int csa2_index_score_topk(const csa2_cache* cache, int mode, const float* iq, co
                                      (hipStream_t)stream));
 }
 
-int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, const uint8_t* swa, int32_t S, const uint16_t* q,
-                       const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws,
-                       size_t ws_bytes, void* stream) {
+int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
+                       const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos, float sm_scale,
+                       uint16_t* out, float* lse, int32_t Q, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_cache(cache, false, true);
   if (rc != CSA2_OK) return rc;
   if (Q < 0 || S < 1) return CSA2_EINVAL;
-  if (cache->batch == 0 || Q == 0) return CSA2_OK;
+  if (swa_x ? (swa_T < 1 || swa_T > S || !swa_len) : (swa_T != 0 || swa_len)) return CSA2_EINVAL;
+  if (cache->batch == 0) return CSA2_OK;
+  if (swa_x && (!swa || !aligned(swa, 16) || !aligned(swa_x, 16) || !aligned(swa_len, 4))) return CSA2_EINVAL;
+  if (Q == 0) {  // no query: only the window append, if any
+    if (!swa_x) return CSA2_OK;
+    return from_hip(csa2::launch_swa_append(swa, S, swa_x, swa_len, cache->batch, swa_T, (hipStream_t)stream));
+  }
   if (!topk || !swa || !q || !out) return CSA2_EINVAL;
-  if (!aligned(topk, 4) || !aligned(swa, 16) || !aligned(q, 16) || !aligned(out, 4)) return CSA2_EINVAL;
+  if (!aligned(topk, 16) || !aligned(swa, 16) || !aligned(q, 16) || !aligned(out, 16)) return CSA2_EINVAL;
   if ((lse && !aligned(lse, 4)) || (q_pos && !aligned(q_pos, 4))) return CSA2_EINVAL;
   const size_t need = csa2_workspace_bytes(CSA2_OP_ATTEND, cache->batch, Q, cache->capacity);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
-  return from_hip(csa2::launch_attend(to_launch(cache), topk, swa, S, q, q_pos, sm_scale, out, lse, Q, ws,
-                                      (hipStream_t)stream));
+  return from_hip(csa2::launch_attend(to_launch(cache), topk, swa, S, swa_x, swa_len, swa_T, q, q_pos, sm_scale, out,
+                                      lse, Q, ws, (hipStream_t)stream));
 }
 
 size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t capacity) {

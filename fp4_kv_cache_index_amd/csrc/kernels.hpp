@@ -60,8 +60,8 @@ hipError_t launch_swa_append(uint8_t* swa, int32_t S, const float* x, const int3
 hipError_t launch_index(const LaunchCache& c, int mode, const float* iq, const float* iw, const int32_t* q_pos,
                         const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws,
                         hipStream_t stream);
-hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, const uint8_t* swa, int32_t S,
-                         const uint16_t* q, const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse,
-                         int32_t Q, void* ws, hipStream_t stream);
+hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
+                         const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos,
+                         float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws, hipStream_t stream);
 
 }  // namespace csa2

@@ -110,9 +110,23 @@ def test_attend_rejections(csa):
     p = ctypes.c_void_p(FAKE)
     a = L.csa2_sparse_attend
     c = ctypes.byref(cache(csa, B=16))
-    assert a(c, p, p, 0, p, None, 1.0, p, None, 1, p, 1 << 40, None) == csa.EINVAL        # S
-    assert a(c, None, p, 128, p, None, 1.0, p, None, 1, p, 1 << 40, None) == csa.EINVAL   # topk
-    assert a(c, p, p, 128, p, None, 1.0, None, None, 1, p, 1 << 40, None) == csa.EINVAL   # out
-    assert a(c, p, p, 128, p, None, 1.0, p, None, 1, p, 8, None) == csa.EWORKSPACE
-    assert a(ctypes.byref(cache(csa, kv_scales=None)), p, p, 128, p, None, 1.0, p, None, 1, p, 1 << 40,
-             None) == csa.EINVAL
+    big_ws = 1 << 40
+    # (cache, topk, swa, S, swa_x, swa_len, swa_T, q, q_pos, sm_scale, out, lse, Q, ws, ws_bytes, stream)
+    assert a(c, p, p, 0, None, None, 0, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL        # S
+    assert a(c, None, p, 128, None, None, 0, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL   # topk
+    assert a(c, p, p, 128, None, None, 0, p, None, 1.0, None, None, 1, p, big_ws, None) == csa.EINVAL   # out
+    assert a(c, p, p, 128, None, None, 0, p, None, 1.0, p, None, 1, p, 8, None) == csa.EWORKSPACE
+    assert a(ctypes.byref(cache(csa, kv_scales=None)), p, p, 128, None, None, 0, p, None, 1.0, p, None, 1, p,
+             big_ws, None) == csa.EINVAL
+    # fused window append: x, its lengths and T come together, 1 <= T <= S
+    assert a(c, p, p, 128, p, None, 1, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL          # no swa_len
+    assert a(c, p, p, 128, p, p, 0, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL             # T = 0
+    assert a(c, p, p, 128, p, p, 129, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL           # T > S
+    assert a(c, p, p, 128, None, p, 0, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL          # stray len
+    assert a(c, p, p, 128, None, None, 3, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL       # stray T
+    odd = ctypes.c_void_p(FAKE + 4)
+    assert a(c, odd, p, 128, None, None, 0, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL     # topk align
+    assert a(c, p, p, 128, odd, p, 1, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL           # x align
+    assert a(c, p, None, 128, p, p, 1, p, None, 1.0, p, None, 1, p, big_ws, None) == csa.EINVAL          # no ring
+    # zero queries and no append: nothing to do
+    assert a(c, None, None, 128, None, None, 0, None, None, 1.0, None, None, 0, None, 0, None) == csa.OK

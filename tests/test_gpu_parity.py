@@ -322,6 +322,74 @@ def test_attend(csa, orc, B, Q, E, S, mode):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("B,Q,E,S,T", [
+    (2, 1, 5000, 128, 1),      # decode: the new token is the query's own position
+    (3, 1, 60, 128, 1),        # short sequences: the window reaches position 0
+    (1, 64, 3000, 192, 64),    # a 64-token chunk appended by the workgroups of 64 queries
+    (2, 2, 9000, 130, 2),      # two queries, ring barely above window + Q - 1
+])
+def test_attend_fused_window_append(csa, orc, B, Q, E, S, T):
+    """The fused append equals csa2_swa_append followed by attention: identical
+    ring bytes and bit-identical outputs, and both match the oracle."""
+    cap = E + 3
+    oc = oracle_cache_full(orc, B, cap, [E] * B, 31)
+    n_after = E + 0  # token positions: ratio 1, the new tokens are E-T .. E-1
+    q_pos = np.array([[n_after - Q + q for q in range(Q)] for _ in range(B)], np.int32)
+    iq = synth.normal(31, "iq", (B, Q, 4, 64))
+    topk, _, _ = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos)
+    # ring before the append: tokens up to n_after - T
+    swa0 = np.zeros((B, S, 512), np.uint8)
+    n_before = n_after - T
+    t0 = max(0, n_before - S)
+    for b in range(B):
+        x = synth.normal_rows(31, "swa", b * 100000 + t0, n_before - t0, 512).reshape(1, -1, 512)
+        sub = np.zeros((1, S, 512), np.uint8)
+        if n_before > t0:
+            orc.swa_append(sub, x, np.array([n_before], np.int32))
+        swa0[b] = sub[0]
+    xs = synth.normal(31, "xnew", (B, T, 512))
+    seq = np.full(B, n_after, np.int32)
+    swa_ref = swa0.copy()
+    orc.swa_append(swa_ref, xs, seq)
+    qf = bf16_round(synth.normal(31, "q", (B, Q, 16, 512)))
+    ref, _ = orc.attend(oc, topk, swa_ref, qf.float().numpy(), SM, q_pos=q_pos)
+
+    gc = upload(csa, oc, with_main=True)
+    # unfused: append, then attend
+    ring_a = dev(swa0)
+    csa.swa_append(ring_a, dev(xs), dev(seq))
+    out_a = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse_a = torch.empty((B, Q, 16), dtype=torch.float32, device="cuda")
+    csa.sparse_attend(gc, dev(topk), ring_a, qf.cuda(), out_a, SM, lse=lse_a, q_pos=dev(q_pos))
+    # fused
+    ring_b = dev(swa0)
+    out_b = torch.empty_like(out_a)
+    lse_b = torch.empty_like(lse_a)
+    csa.sparse_attend(gc, dev(topk), ring_b, qf.cuda(), out_b, SM, lse=lse_b, q_pos=dev(q_pos),
+                      swa_x=dev(xs), swa_len=dev(seq))
+    assert np.array_equal(host(ring_b), swa_ref)
+    assert np.array_equal(host(ring_a), swa_ref)
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(lse_a, lse_b)
+    attn_close(host(out_b.float()), ref, name="fused")
+
+
+def test_attend_fused_append_without_queries(csa, orc):
+    """Q = 0 with new window tokens: the call only appends."""
+    B, S, T = 2, 128, 3
+    gc = csa.Cache(B, 16, 1)
+    xs = synth.normal(32, "x", (B, T, 512))
+    seq = np.array([T, 200], np.int32)
+    ref = np.zeros((B, S, 512), np.uint8)
+    orc.swa_append(ref, xs, seq)
+    ring = torch.zeros((B, S, 512), dtype=torch.uint8, device="cuda")
+    q = torch.empty((B, 0, 16, 512), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    topk = torch.empty((B, 0, 512), dtype=torch.int32, device="cuda")
+    csa.sparse_attend(gc, topk, ring, q, out, SM, swa_x=dev(xs), swa_len=dev(seq))
+    assert np.array_equal(host(ring), ref)
+
+
 # ------------------------------------------------------------------ step
 def test_decode_group_step_small(csa, orc):
     """Full(+pool) -> Reindex -> Reuse -> Reuse decode steps on a small cache,
@@ -351,8 +419,10 @@ def test_decode_group_step_small(csa, orc):
         for l, mode in enumerate(("full_pool", "reindex", "reuse", "reuse")):
             xs = synth.normal(42, f"x{step}_{l}", (B, 1, 512))
             orc.swa_append(swa_o[l], xs, seq_o)
-            csa.swa_append(swa_g[l], dev(xs), gc.length)
-            assert np.array_equal(host(swa_g[l]), swa_o[l])
+            fused = l % 2 == 0  # even layers append inside the attention call
+            if not fused:
+                csa.swa_append(swa_g[l], dev(xs), gc.length)
+                assert np.array_equal(host(swa_g[l]), swa_o[l])
             iq = synth.normal(43, f"iq{step}_{l}", (B, 1, 4, 64))
             if mode == "full_pool":
                 ref, pool_o, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
@@ -372,5 +442,9 @@ def test_decode_group_step_small(csa, orc):
             qf = bf16_round(synth.normal(44, f"q{step}_{l}", (B, 1, 16, 512)))
             ref_o, _ = orc.attend(oc, topk_prev, swa_o[l], qf.float().numpy(), SM)
             out = torch.empty((B, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
-            csa.sparse_attend(gc, dev(topk_prev), swa_g[l], qf.cuda(), out, SM)
+            if fused:
+                csa.sparse_attend(gc, dev(topk_prev), swa_g[l], qf.cuda(), out, SM, swa_x=dev(xs), swa_len=gc.length)
+                assert np.array_equal(host(swa_g[l]), swa_o[l])
+            else:
+                csa.sparse_attend(gc, dev(topk_prev), swa_g[l], qf.cuda(), out, SM)
             attn_close(host(out.float()), ref_o, name=f"step {step} layer {l}")
