@@ -1,5 +1,5 @@
 // Workgroup-wide building blocks for the selection kernels: reductions,
-// exclusive scan, exact K-th-largest selection and bitonic sort.  All operate on
+// exclusive scan and exact top-k thresholds.  All operate on
 // LDS data and must be called by every thread of the workgroup (blockDim a
 // multiple of 64, at most 1024).
 #pragma once
@@ -8,41 +8,79 @@
 
 namespace csa2 {
 
+// ---- wave-wide primitives on DPP (cross-lane moves inside the VALU; the
+// __shfl family goes through the LDS crossbar with its latency)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each row of 16
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;  // row_shr:n
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, true);
+}
+template <int Ctrl>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return (uint64_t)dpp32<Ctrl>((uint32_t)v) | ((uint64_t)dpp32<Ctrl>((uint32_t)(v >> 32)) << 32);
+}
+template <int Ctrl, typename T>
+__device__ __forceinline__ T dpp(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, dpp64<Ctrl>(__builtin_bit_cast(uint64_t, v)));
+  else return __builtin_bit_cast(T, dpp32<Ctrl>(__builtin_bit_cast(uint32_t, v)));
+}
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int l) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(T, (uint64_t)lo | ((uint64_t)hi << 32));
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  }
+}
+
+// Reduce over the wave with a commutative, associative op; every lane gets the result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppMirror>(v));  // every lane holds its row's result
+  return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
+}
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](T x, T y) { return x + y; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const T y = __shfl_xor(v, o);
-    v = y < v ? y : v;
-  }
-  return v;
+  return wave_reduce(v, [](T x, T y) { return y < x ? y : x; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const T y = __shfl_xor(v, o);
-    v = y > v ? y : v;
-  }
-  return v;
+  return wave_reduce(v, [](T x, T y) { return y > x ? y : x; });
+}
+
+// Inclusive prefix sum over the 64 lanes (lane 0 first), 32-bit.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp32<kDppShr1>(x);  // out-of-row sources read 0
+  x += dpp32<kDppShr2>(x);
+  x += dpp32<kDppShr4>(x);
+  x += dpp32<kDppShr8>(x);  // inclusive scan inside each row of 16
+  const uint32_t r0 = readlane(x, 15), r1 = readlane(x, 31), r2 = readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 // Exclusive prefix sum of one int per thread over the workgroup; `tmp` holds
 // one int per wave.  Returns the exclusive prefix, writes the total to *total.
 __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -72,83 +110,47 @@ __device__ __forceinline__ int block_offsets(const int* v, int* off, int n, int*
 }
 
 struct SelShared {
-  uint32_t red[16][8];
+  uint32_t hist[256];
   uint64_t wmin[16], wmax[16];
+  uint32_t wcnt[16];
   uint64_t small[64];
   uint64_t kbc[2];
   int ibc[6];
 };
 
-// Sum each of eight per-lane words over the wave by reduce-scatter (10
-// shuffles): lane l ends up with the total of word (l >> 3) & 7.
-__device__ __forceinline__ uint32_t wave_reduce8(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t c4,
-                                                 uint32_t c5, uint32_t c6, uint32_t c7) {
-  const int lane = threadIdx.x & 63;
-  const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
-  const uint32_t v0 = (h32 ? c4 : c0) + __shfl_xor(h32 ? c0 : c4, 32);
-  const uint32_t v1 = (h32 ? c5 : c1) + __shfl_xor(h32 ? c1 : c5, 32);
-  const uint32_t v2 = (h32 ? c6 : c2) + __shfl_xor(h32 ? c2 : c6, 32);
-  const uint32_t v3 = (h32 ? c7 : c3) + __shfl_xor(h32 ? c3 : c7, 32);
-  const uint32_t w0 = (h16 ? v2 : v0) + __shfl_xor(h16 ? v0 : v2, 16);
-  const uint32_t w1 = (h16 ? v3 : v1) + __shfl_xor(h16 ? v1 : v3, 16);
-  uint32_t u = (h8 ? w1 : w0) + __shfl_xor(h8 ? w0 : w1, 8);
-  u += __shfl_xor(u, 4);
-  u += __shfl_xor(u, 2);
-  u += __shfl_xor(u, 1);
-  return u;
-}
-
-// Descending bitonic sort of one value per lane across the wave.
-template <typename Key>
-__device__ __forceinline__ Key wave_sort_desc(Key v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const Key y = __shfl_xor(v, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0;  // this k-block sorts descending
-      const bool take_max = (lower == desc);
-      v = take_max ? (y > v ? y : v) : (y < v ? y : v);
-    }
-  }
-  return v;
-}
-
-// Exact K-th largest of the eligible keys among a[0..n) (1 <= k <= number of
-// eligible keys, n < 65536; keys equal to 0 are not eligible when skip_zero).
-// Returns the key value T; *rem receives how many keys equal to T complete the
-// top k (the keys greater than T are k - *rem).
+// Threshold of the top k among unique keys get(0) .. get(n-1), where a key of 0
+// marks "no key": returns T such that exactly min(k, number of nonzero keys)
+// keys are >= T (T = 1 when there are at most k).  *n_keys receives the number
+// of nonzero keys.  `get` reads LDS (or registers) and is called many times.
 //
-// Most-significant-digit radix select with 4-bit digits.  Each thread counts
-// its keys into 16 counters held in registers (two 16-bit counters per word),
-// a reduce-scatter sums them over the wave and LDS over the workgroup, and the
-// digit holding the k-th key fixes 4 more bits.  Leading bits common to all
-// eligible keys are skipped; once the bucket holding the k-th key has at most
-// 64 keys, one wave sorts it and reads the answer off directly.
-template <typename Key>
-__device__ Key select_kth_largest(const Key* a, int n, int k, bool skip_zero, SelShared& S, int* rem) {
+// Most-significant-digit radix select.  The bits above the highest bit in which
+// the keys differ are fixed at once; each pass then counts the next 8 bits of
+// the keys still in the running into a 256-bin LDS histogram (atomic adds), and
+// one wave finds the digit that holds the k-th key.  Once that bucket has at
+// most 64 keys, one wave ranks them and the key of rank k is the answer.
+template <typename Key, typename Get>
+__device__ Key topk_threshold(Get get, int n, int k, SelShared& S, int* n_keys) {
   constexpr int kBits = (int)sizeof(Key) * 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  // ---- common prefix and count of all eligible keys
+  // ---- common prefix and count of the keys
   Key lo = ~(Key)0, hi = 0;
-  int cnt_el = 0;
+  int cnt = 0;
   for (int i = tid; i < n; i += blockDim.x) {
-    const Key x = a[i];
-    if (skip_zero && x == 0) continue;
+    const Key x = get(i);
+    if (x == 0) continue;
     lo = x < lo ? x : lo;
     hi = x > hi ? x : hi;
-    cnt_el++;
+    cnt++;
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
-  cnt_el = wave_sum(cnt_el);
+  cnt = wave_sum(cnt);
   if (lane == 0) {
     S.wmin[wave] = (uint64_t)lo;
     S.wmax[wave] = (uint64_t)hi;
-    S.red[wave][0] = (uint32_t)cnt_el;
+    S.wcnt[wave] = (uint32_t)cnt;
   }
+  for (int i = tid; i < 256; i += blockDim.x) S.hist[i] = 0u;
   __syncthreads();
   {
     Key l = ~(Key)0, h = 0;
@@ -156,64 +158,51 @@ __device__ Key select_kth_largest(const Key* a, int n, int k, bool skip_zero, Se
     for (int w = 0; w < nw; w++) {
       l = (Key)S.wmin[w] < l ? (Key)S.wmin[w] : l;
       h = (Key)S.wmax[w] > h ? (Key)S.wmax[w] : h;
-      c += (int)S.red[w][0];
+      c += (int)S.wcnt[w];
     }
     lo = l;
     hi = h;
-    cnt_el = c;
+    cnt = c;
   }
-  __syncthreads();
-  const Key diff = lo ^ hi;
-  if (diff == 0) {
-    *rem = k;
-    return hi;
-  }
-  const int lead = kBits == 64 ? __clzll((long long)diff) : __clz((int)diff);
-  const int top = kBits - (lead / 4) * 4;  // bits [0, top) may differ
+  __syncthreads();  // every thread has read S.wmin/wmax/wcnt
+  *n_keys = cnt;
+  if (cnt <= k) return (Key)1;
+  const Key diff = lo ^ hi;  // nonzero: the keys are unique and there are more than k >= 1
+  int top = kBits - (kBits == 64 ? __clzll((long long)diff) : __clz((int)diff));  // bits [0, top) differ
   Key mask = top >= kBits ? (Key)0 : (Key)(~(Key)0 << top);
   Key prefix = hi & mask;
-  int bucket = cnt_el;  // keys under the current prefix
-  int shift = top;
-  while (bucket > 64 && shift > 0) {
-    shift -= 4;
-    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0, c4 = 0, c5 = 0, c6 = 0, c7 = 0;
+  int bucket = cnt;  // keys under the current prefix
+  while (bucket > 64 && top > 0) {
+    const int width = top < 8 ? top : 8;
+    const int shift = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    // the histogram is zero here: cleared before the first pass, and by its
+    // reader after each pass
     for (int i = tid; i < n; i += blockDim.x) {
-      const Key x = a[i];
-      if ((skip_zero && x == 0) || (x & mask) != prefix) continue;
-      const uint32_t d = (uint32_t)(x >> shift) & 15u;
-      const uint32_t inc = 1u << ((d & 1u) * 16);
-      const uint32_t w = d >> 1;
-      c0 += w == 0 ? inc : 0u;
-      c1 += w == 1 ? inc : 0u;
-      c2 += w == 2 ? inc : 0u;
-      c3 += w == 3 ? inc : 0u;
-      c4 += w == 4 ? inc : 0u;
-      c5 += w == 5 ? inc : 0u;
-      c6 += w == 6 ? inc : 0u;
-      c7 += w == 7 ? inc : 0u;
+      const Key x = get(i);
+      if (x == 0 || (x & mask) != prefix) continue;
+      atomicAdd(&S.hist[(uint32_t)(x >> shift) & dmask], 1u);
     }
-    const uint32_t tot = wave_reduce8(c0, c1, c2, c3, c4, c5, c6, c7);
-    if ((lane & 7) == 0) S.red[wave][lane >> 3] = tot;
     __syncthreads();
     if (wave == 0) {
-      // lane j (< 16) owns digit j: its count, then the count of all larger digits
-      uint32_t cnt = 0;
-      if (lane < 16) {
-        uint32_t s = 0;
-        for (int w = 0; w < nw; w++) s += S.red[w][lane >> 1];
-        cnt = (lane & 1) ? (s >> 16) : (s & 0xFFFFu);
-      }
-      uint32_t incl = cnt;  // sum over digits >= lane
+      // lane l owns digits 255-4l .. 252-4l, so a prefix sum over the lanes
+      // counts the keys in all digits above a lane's four
+      uint32_t c[4];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const uint32_t y = __shfl_down(incl, o, 16);
-        if (lane + o < 16) incl += y;
+      for (int j = 0; j < 4; j++) {
+        c[j] = S.hist[255 - 4 * lane - j];
+        S.hist[255 - 4 * lane - j] = 0u;
       }
-      const int above = (int)(incl - cnt);
-      if (lane < 16 && above < k && (int)incl >= k) {
-        S.ibc[0] = lane;
-        S.ibc[1] = k - above;
-        S.ibc[2] = (int)cnt;
+      const uint32_t own = c[0] + c[1] + c[2] + c[3];
+      uint32_t above = wave_incl_scan(own) - own;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {  // this lane's digits, descending
+        if ((int)above < k && (int)(above + c[j]) >= k) {
+          S.ibc[0] = 255 - 4 * lane - j;
+          S.ibc[1] = k - (int)above;
+          S.ibc[2] = (int)c[j];
+        }
+        above += c[j];
       }
     }
     __syncthreads();
@@ -221,58 +210,32 @@ __device__ Key select_kth_largest(const Key* a, int n, int k, bool skip_zero, Se
     k = S.ibc[1];
     bucket = S.ibc[2];
     prefix |= (Key)d << shift;
-    mask |= (Key)15 << shift;
+    mask |= (Key)dmask << shift;
+    top = shift;
     __syncthreads();
   }
-  if (shift == 0) {  // the prefix is the whole key
-    *rem = k;
-    return prefix;
-  }
-  // ---- small bucket: gather it and let one wave sort it
+  if (top == 0) return prefix;  // every bit fixed (only unique keys reach here with bucket <= 1)
+  // ---- small bucket: gather it and let one wave rank it
   if (tid == 0) S.ibc[3] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
-    const Key x = a[i];
-    if ((skip_zero && x == 0) || (x & mask) != prefix) continue;
-    S.small[atomicAdd(&S.ibc[3], 1)] = (uint64_t)x;
+    const Key x = get(i);
+    if (x == 0 || (x & mask) != prefix) continue;
+    const int slot = atomicAdd(&S.ibc[3], 1);
+    if (slot < 64) S.small[slot] = (uint64_t)x;
   }
   __syncthreads();
   if (wave == 0) {
-    Key v = lane < bucket ? (Key)S.small[lane] : (Key)0;
-    v = wave_sort_desc<Key>(v);
-    const Key t = __shfl(v, k - 1);
-    const uint64_t gt = __ballot(lane < bucket && v > t);
-    if (lane == 0) {
-      S.kbc[0] = (uint64_t)t;
-      S.ibc[4] = k - __popcll(gt);
-    }
+    // rank each key of the bucket against all of them (broadcast LDS reads)
+    const Key v = lane < bucket ? (Key)S.small[lane] : (Key)0;
+    int greater = 0;
+    for (int j = 0; j < bucket; j++) greater += (Key)S.small[j] > v;
+    if (lane < bucket && greater == k - 1) S.kbc[0] = (uint64_t)v;
   }
   __syncthreads();
   const Key t = (Key)S.kbc[0];
-  *rem = S.ibc[4];
   __syncthreads();
   return t;
-}
-
-// Bitonic sort of n (power of two) keys in LDS, descending or ascending.
-template <typename Key, bool Descending>
-__device__ void bitonic_sort(Key* a, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (j - 1));
-        const int hi = lo + j;
-        const Key x = a[lo], y = a[hi];
-        const bool up = (lo & k) == 0;  // this segment's target direction
-        const bool swap = Descending ? (up ? x < y : x > y) : (up ? x > y : x < y);
-        if (swap) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 }  // namespace csa2
