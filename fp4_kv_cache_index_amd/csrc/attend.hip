@@ -29,6 +29,7 @@
 // on gfx950 than the second launch.)
 #include <hip/hip_runtime.h>
 
+#include "block_ops.hpp"
 #include "codec.hpp"
 #include "kernels.hpp"
 
@@ -42,6 +43,7 @@ constexpr int kThreads = 256;
 constexpr int kKStride = 520;  // fp16 per key row of the [key][dim] tile (512 + pad)
 constexpr int kVStride = 40;   // fp16 per dim row of the [dim][key] tile (32 keys + pad)
 constexpr int kPStride = 40;
+constexpr int kRedStride = 80;  // 64 lanes + pad: the four row groups start 16 banks apart
 constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
 constexpr int kMaxSplits = 10;
 
@@ -115,8 +117,7 @@ __device__ __forceinline__ uint4 encode16(const float* x) {
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[kAttnTile * kKStride];
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[512 * kVStride];
-  __shared__ float s_red[4][2][256];
-  __shared__ float s_sfull[16][kAttnTile];
+  __shared__ float s_red[4][2][4][kRedStride];  // [wave][key block][row group i][lane]
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * kPStride];
   __shared__ float s_m[16], s_l[16], s_alpha[16];
   __shared__ float s_qmax[4][16];
@@ -214,10 +215,6 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (lane < 16) s_qmax[wave][lane] = amax;
-    if (tid < 16) {
-      s_m[tid] = -INFINITY;
-      s_l[tid] = 0.0f;
-    }
     __syncthreads();
     const int h = lane & 15;
     const float hmax = fmaxf(fmaxf(s_qmax[0][h], s_qmax[1][h]), fmaxf(s_qmax[2][h], s_qmax[3][h]));
@@ -235,6 +232,12 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   v4f acc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ct++) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // online softmax state: thread tid serves head tid/16 (its 16 threads are one
+  // DPP row and all hold the head's running max and sum)
+  const int sm_h = tid >> 4;
+  float m_run = -INFINITY, l_run = 0.0f;
+  __syncthreads();  // s_qfac is written
+  const float qfac = s_qfac[sm_h];
 
   for (int tile = t_begin; tile < t_end; tile++) {
     // prefetch the next tile's rows and the indices of the one after
@@ -299,42 +302,31 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], __builtin_bit_cast(v8h, x), sacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++) s_red[wave][th][i * 64 + lane] = sacc[i];
+      for (int i = 0; i < 4; i++) s_red[wave][th][i][lane] = sacc[i];
     }
     __syncthreads();
-    // reduce the four waves: element (th, i, lane) is head 4*(lane/16)+i, key 16*th + lane%16
-    for (int x = tid; x < 512; x += kThreads) {
-      const int th = x >> 8, i = (x >> 6) & 3, l = x & 63;
-      const float sv = s_red[0][th][i * 64 + l] + s_red[1][th][i * 64 + l] + s_red[2][th][i * 64 + l] +
-                       s_red[3][th][i * 64 + l];
-      const int head = 4 * (l >> 4) + i, key = 16 * th + (l & 15);
-      // the head's factor undoes its query scale exactly and applies sm_scale
-      s_sfull[head][key] = s_valid[key] ? sv * s_qfac[head] : -INFINITY;
-    }
-    __syncthreads();
-    // ---------------- online softmax: 16 threads per head, 2 keys each
+    // ---------------- scores (the four waves' partial sums) and online softmax:
+    // thread (head h, keys 2j, 2j+1); partial element (th, i, lane) is head
+    // 4*(lane/16)+i, key 16*th + lane%16
     {
-      const int h = tid >> 4, k0 = 2 * (tid & 15);
-      const float a0 = s_sfull[h][k0], a1 = s_sfull[h][k0 + 1];
-      float mt = fmaxf(a0, a1);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 16));
-      const float m_old = s_m[h];
-      const float m_new = fmaxf(m_old, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_old - m_new);
+      const int h = sm_h, k0 = 2 * (tid & 15);
+      const int th = k0 >> 4, l = 16 * (h >> 2) + (k0 & 15), i = h & 3;
+      const float s0 = s_red[0][th][i][l] + s_red[1][th][i][l] + s_red[2][th][i][l] + s_red[3][th][i][l];
+      const float s1 = s_red[0][th][i][l + 1] + s_red[1][th][i][l + 1] + s_red[2][th][i][l + 1] + s_red[3][th][i][l + 1];
+      // the head's factor undoes its query scale exactly and applies sm_scale
+      const float a0 = s_valid[k0] ? s0 * qfac : -INFINITY;
+      const float a1 = s_valid[k0 + 1] ? s1 * qfac : -INFINITY;
+      const float mt = wave_row_reduce(fmaxf(a0, a1), [](float x, float y) { return fmaxf(x, y); });
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
       const float p0 = (a0 == -INFINITY) ? 0.0f : __expf(a0 - m_new);
       const float p1 = (a1 == -INFINITY) ? 0.0f : __expf(a1 - m_new);
-      float ps = p0 + p1;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 16);
+      const float ps = wave_row_reduce(p0 + p1, [](float x, float y) { return x + y; });
       s_p[h * kPStride + k0] = (_Float16)p0;
       s_p[h * kPStride + k0 + 1] = (_Float16)p1;
-      __syncthreads();  // every thread has read s_m before it changes
-      if ((tid & 15) == 0) {
-        s_m[h] = m_new;
-        s_l[h] = alpha * s_l[h] + ps;
-        s_alpha[h] = alpha;
-      }
+      m_run = m_new;
+      l_run = alpha * l_run + ps;
+      if ((tid & 15) == 0) s_alpha[h] = alpha;
     }
     __syncthreads();
     // ---------------- O = alpha * O + P V
@@ -361,6 +353,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   }
 
   // ---------------- epilogue: rows 4*(lane/16)+i are heads, column lane%16 a dim
+  if ((tid & 15) == 0) {
+    s_m[sm_h] = m_run;
+    s_l[sm_h] = l_run;
+  }
+  __syncthreads();
   if (a.splits == 1) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {

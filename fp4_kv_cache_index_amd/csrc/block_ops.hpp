@@ -52,6 +52,14 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
   v = op(v, dpp<kDppMirror>(v));  // every lane holds its row's result
   return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
 }
+// Reduce over each DPP row of 16 lanes; every lane gets its row's result.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_row_reduce(T v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  return op(v, dpp<kDppMirror>(v));
+}
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
   return wave_reduce(v, [](T x, T y) { return x + y; });
