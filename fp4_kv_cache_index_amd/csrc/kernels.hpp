@@ -29,23 +29,21 @@ constexpr int kPool = kPoolBlocks * kBlock;
 inline int64_t full_chunks(int32_t capacity) { return ((int64_t)capacity + kFullChunk - 1) / kFullChunk; }
 inline int64_t reindex_chunks() { return kPool / kReindexChunk; }
 
-// Workspace of one index call, per (sequence, query) and chunk: the chunk's
-// Top-512 u64 keys and their top-m summary, the chunk's block-maximum keys and
-// their summary (all unordered), and the counts.
+// Workspace of one index call.  The first three planes must be zero when a
+// call starts and are left zero when it ends; their offsets depend only on the
+// number of queries, so Full and Reindex calls can share one workspace.
 struct IndexWs {
-  uint64_t* lists;    // [BQ][chunks][512]
-  uint64_t* summ;     // [BQ][chunks][512] (first min(count, m) used)
-  uint32_t* counts;   // [BQ][chunks]
-  uint64_t* blists;   // [BQ][chunks][chunk/8]
-  uint64_t* bsumm;    // [BQ][chunks][chunk/8]
-  uint32_t* bcounts;  // [BQ][chunks]
+  uint32_t* count;  // [BQ][2] candidates found (entries, blocks)
+  uint32_t* fine;   // [BQ][2][256] next 8 bits of the keys in the boundary bin
+  uint32_t* hist;   // [BQ][2][4096] top 12 bits of the score keys
+  uint64_t* cand;   // [BQ][2][8192] candidate u64 keys
+  uint32_t* keys;   // [BQ][slots] score key of every entry (Full) or pool slot (Reindex)
+  uint32_t* bkeys;  // [BQ][slots / 8] block-maximum keys (Full with a pool)
+  int64_t slots;
 };
-// summary length for lists of `per_list` keys from which the top `k` overall
-// are selected over `n_lists` lists: the mean share plus four standard
-// deviations (rarely exceeded by i.i.d. scores), bounded by what one merge stages
-int summary_len(int k, int64_t n_lists, int per_list, int cap);
+int64_t index_slots(int32_t capacity);
 size_t index_ws_bytes(int64_t bq, int32_t capacity);
-IndexWs index_ws_carve(void* ws, int64_t bq, int64_t chunks, int chunk);
+IndexWs index_ws_carve(void* ws, int64_t bq, int32_t capacity);
 
 // ---- attention geometry
 constexpr int kAttnKeys = 640;  // 512 selected + 128 window
