@@ -84,6 +84,20 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// Slot from an LDS counter for every lane whose `pred` holds, with one atomic
+// per wave; the lanes get consecutive slots in lane order.  Every lane of the
+// wave must call it (returns -1 where pred is false).
+__device__ __forceinline__ int wave_slot(bool pred, int* counter) {
+  const uint64_t mask = __ballot(pred);
+  if (mask == 0ull) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(mask));
+  base = __builtin_amdgcn_readlane(base, leader);
+  return pred ? base + __popcll(mask & ((1ull << lane) - 1ull)) : -1;
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup; `tmp` holds
 // one int per wave.  Returns the exclusive prefix, writes the total to *total.
 __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {
