@@ -98,6 +98,18 @@ __device__ __forceinline__ int wave_slot(bool pred, int* counter) {
   return pred ? base + __popcll(mask & ((1ull << lane) - 1ull)) : -1;
 }
 
+// Reserve `count` consecutive slots per lane from an LDS counter with one
+// atomic per wave; returns this lane's first slot (lanes in order).  Every lane
+// of the wave must call it.
+__device__ __forceinline__ int wave_alloc(int count, int* counter) {
+  const uint32_t incl = wave_incl_scan((uint32_t)count);
+  const uint32_t total = readlane(incl, 63);
+  int base = 0;
+  if ((threadIdx.x & 63) == 0 && total) base = atomicAdd(counter, (int)total);
+  base = __builtin_amdgcn_readlane(base, 0);
+  return base + (int)incl - count;
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup; `tmp` holds
 // one int per wave.  Returns the exclusive prefix, writes the total to *total.
 __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {
