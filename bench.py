@@ -296,24 +296,30 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
         # the calibration copies are the last three device copies of the run
         return acc, [v for _, v in sorted(copies)[-3:]]
 
+    # the kernels of one Full call: score, filter (only the Full call launches it
+    # at this workload) and final (the Full call's has the larger grid: it also
+    # builds the pool)
+    def full_call(acc, name, largest_grid=False):
+        grids = [g for (n, g) in acc if name in n]
+        return [v for (n, g), vals in acc.items()
+                if name in n and (not largest_grid or g == max(grids)) for v in vals]
+
+    parts = (("score", "index_score_kernel<4096, false>", False), ("filter", "index_filter_kernel", False),
+             ("final", "index_final_kernel", True))
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc, copy = per_kernel(path, counter)
-        scan = [v for (n, g), vals in acc.items() if "index_scan_kernel<4096, false>" in n for v in vals]
-        # the Full call's merge has twice the workgroups of the Reindex merge
-        merge_grids = [g for (n, g) in acc if "index_merge_kernel" in n]
-        merge = [v for (n, g), vals in acc.items() if "index_merge_kernel" in n and merge_grids and
-                 g == max(merge_grids) for v in vals]
         kib_copy = float(np.median(copy)) if copy else float("nan")
-        factor = COPY_BYTES / (kib_copy * 1024.0)
         key = "fetch" if counter == "FETCH_SIZE" else "write"
-        out[f"{key}_kib_scan"] = float(np.mean(scan)) if scan else None
-        out[f"{key}_kib_merge"] = float(np.mean(merge)) if merge else None
+        for part, name, largest in parts:
+            vals = full_call(acc, name, largest)
+            out[f"{key}_kib_{part}"] = float(np.mean(vals)) if vals else None
         out[f"{key}_kib_copy_{COPY_BYTES >> 20}MiB"] = kib_copy
-        out[f"{key}_factor"] = factor
+        out[f"{key}_factor"] = COPY_BYTES / (kib_copy * 1024.0)
     tot = 0.0
     for key in ("fetch", "write"):
-        tot += ((out[f"{key}_kib_scan"] or 0.0) + (out[f"{key}_kib_merge"] or 0.0)) * 1024.0 * out[f"{key}_factor"]
+        kib = sum(out[f"{key}_kib_{part}"] or 0.0 for part, _, _ in parts)
+        tot += kib * 1024.0 * out[f"{key}_factor"]
     src = "index.hip"
     sha = hashlib.sha256(open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", src), "rb").read()).hexdigest()
     out.update(source=src, source_sha256=sha, workload=workload_name, hbm_bytes_per_launch=round(tot))
@@ -434,7 +440,7 @@ def main():
     traffic = traffic_from_profiles(wl, "index_full")
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
                 frac=round(achieved / PEAK_GBPS, 4), traffic=traffic,
-                kernel="index_scan_kernel<4096> + index_merge_kernel (one csa2_index_score_topk Full call)",
+                kernel="index_score + index_filter + index_final (one csa2_index_score_topk Full call)",
                 bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
     log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
 
