@@ -199,7 +199,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     uint4 qraw[4];
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) qraw[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-    load_tile(t_begin, ec, wc, vc);  // the first tile's rows load while the query is scaled
+    // the first two tiles' rows load while the query is scaled
+    load_tile(t_begin, ec, wc, vc);
+    if (t_begin + 1 < t_end) load_tile(t_begin + 1, en, wn, vn);
     float qf[4][8];
     float amax = 0.0f;
 #pragma unroll
@@ -240,9 +242,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   const float qfac = s_qfac[sm_h];
 
   for (int tile = t_begin; tile < t_end; tile++) {
-    // prefetch the next tile's rows and the indices of the one after
+    // prefetch the next tile's rows (the first workgroup tile's next came with
+    // the query) and the indices of the one after
     const int4 e2 = load_idx(tile + 2);
-    if (tile + 1 < t_end) load_tile(tile + 1, en, wn, vn);
+    if (tile > t_begin && tile + 1 < t_end) load_tile(tile + 1, en, wn, vn);
     // ---------------- dequantise this tile's keys into LDS (fp16, both layouts)
     {
       uint32_t hv[4][8];  // key i: channel pairs (2m, 2m+1) of the group, as fp16x2
