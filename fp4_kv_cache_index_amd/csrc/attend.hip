@@ -14,14 +14,16 @@
 //     exactly and one v_pk_mul_f16 by the group scale gives x = code * scale,
 //     exact in fp16 (at most 6 significant bits, |x| in [2^-10, 2688]); window
 //     bytes widen exactly with v_cvt_scalef32_pk_f16_fp8.  The tile lands in
-//     LDS as fp16 [key][dim] for Q.K^T and fp16 [dim][key] for P.V;
+//     LDS once, as fp16 [key][dim];
 //   S = Q K^T on v_mfma_f32_16x16x32_f16: the bf16 query is scaled per head by
 //     a power of two that puts its largest element in [2^14, 2^15), which makes
 //     the fp16 copy exact for every element within 2^-28 of the head's largest,
 //     and the scores are scaled back exactly (16 heads = the 16 MFMA rows; wave
 //     w covers dims 128w..128w+127 and the four partial S are summed in LDS);
 //   online softmax in fp32 (running max and sum per head);
-//   O += P V on v_mfma_f32_16x16x32_f16, wave w owning output dims 128w.. .
+//   O += P V on v_mfma_f32_16x16x32_f16, wave w owning output dims 128w..; the
+//     V operand (8 keys of one dim per lane) comes straight from the [key][dim]
+//     tile through the LDS transpose read ds_read_b64_tr_b16.
 // With several splits per query the unnormalised partials (O, max, sum) go to
 // the workspace and a second kernel merges them by log-sum-exp weights, one
 // workgroup per (query, head).  (Merging in the last workgroup of each query
@@ -38,14 +40,23 @@ namespace csa2 {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// LDS transpose read: in each 16-lane group, lane 4j+q names 4 consecutive fp16
+// of row j; lane i receives element i%4 of lanes i/4, i/4+4, i/4+8, i/4+12,
+// i.e. column i of the 4-row block.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4h lds_read_tr16(const _Float16* p) {
+  return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
+}
 
 constexpr int kThreads = 256;
-constexpr int kKStride = 520;  // fp16 per key row of the [key][dim] tile (512 + pad)
-constexpr int kVStride = 40;   // fp16 per dim row of the [dim][key] tile (32 keys + pad)
+constexpr int kKStride = 528;  // fp16 per key row of the [key][dim] tile (512 + pad)
 constexpr int kPStride = 40;
 constexpr int kRedStride = 80;  // 64 lanes + pad: the four row groups start 16 banks apart
 constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
 constexpr int kMaxSplits = 10;
+constexpr int kFusedAppendMax = 16;  // new window tokens per sequence appended inside the attention launch
 
 int attend_splits(int64_t bq) {
   int64_t s = (256 + bq - 1) / bq;
@@ -116,7 +127,6 @@ __device__ __forceinline__ uint4 encode16(const float* x) {
 
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[kAttnTile * kKStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vt[512 * kVStride];
   __shared__ float s_red[4][2][4][kRedStride];  // [wave][key block][row group i][lane]
   __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * kPStride];
   __shared__ float s_m[16], s_l[16], s_alpha[16];
@@ -277,16 +287,6 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
         dst[0] = make_uint4(hv[i][0], hv[i][1], hv[i][2], hv[i][3]);
         dst[1] = make_uint4(hv[i][4], hv[i][5], hv[i][6], hv[i][7]);
       }
-      // [dim][key]: channel 16grp+c, keys 4kg .. 4kg+3
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        const uint32_t lo01 = (hv[0][m] & 0xFFFFu) | (hv[1][m] << 16);
-        const uint32_t lo23 = (hv[2][m] & 0xFFFFu) | (hv[3][m] << 16);
-        const uint32_t hi01 = (hv[0][m] >> 16) | (hv[1][m] & 0xFFFF0000u);
-        const uint32_t hi23 = (hv[2][m] >> 16) | (hv[3][m] & 0xFFFF0000u);
-        *reinterpret_cast<uint2*>(s_vt + (16 * grp + 2 * m) * kVStride + 4 * kg) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(s_vt + (16 * grp + 2 * m + 1) * kVStride + 4 * kg) = make_uint2(hi01, hi23);
-      }
     }
     if (grp == 0) {
 #pragma unroll
@@ -339,13 +339,19 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
       float al[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) al[i] = s_alpha[4 * (lane >> 4) + i];
+      // V operand of lane (group G = lane/16, column i = lane%16): keys 8G..8G+7 of
+      // dim 128*wave + 16*ct + i; lane 4j+q of the group names row 8G+j (then
+      // 8G+4+j), dims 4q..4q+3 of the block
+      const _Float16* vsrc =
+          s_k + (8 * (lane >> 4) + ((lane & 15) >> 2)) * kKStride + 128 * wave + 4 * (lane & 3);
 #pragma unroll
       for (int ct = 0; ct < 8; ct++) {
 #pragma unroll
         for (int i = 0; i < 4; i++) acc[ct][i] *= al[i];
-        const int dim = 128 * wave + 16 * ct + (lane & 15);
-        const uint4 kx = *reinterpret_cast<const uint4*>(s_vt + dim * kVStride + 8 * (lane >> 4));
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, __builtin_bit_cast(v8h, kx), acc[ct], 0, 0, 0);
+        const v4h lo = lds_read_tr16(vsrc + 16 * ct);
+        const v4h hi = lds_read_tr16(vsrc + 4 * kKStride + 16 * ct);
+        const v8h vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, vb, acc[ct], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -434,6 +440,16 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
                          float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws, hipStream_t stream) {
   const int64_t bq = (int64_t)c.batch * Q;
   if (bq == 0) return hipSuccess;
+  // A long append (a prefill chunk) goes first as its own launch: inside the
+  // attention kernel every new token would be re-encoded by each of the up to
+  // 128 queries whose window holds it.  The result is the same either way.
+  if (swa_x && swa_T > kFusedAppendMax) {
+    const hipError_t e = launch_swa_append(swa, S, swa_x, swa_len, c.batch, swa_T, stream);
+    if (e != hipSuccess) return e;
+    swa_x = nullptr;
+    swa_len = nullptr;
+    swa_T = 0;
+  }
   AttnArgs a;
   a.kv_codes = c.kv_codes;
   a.kv_scales = c.kv_scales;
