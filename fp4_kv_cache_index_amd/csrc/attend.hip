@@ -56,7 +56,7 @@ constexpr int kPStride = 40;
 constexpr int kRedStride = 80;  // 64 lanes + pad: the four row groups start 16 banks apart
 constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
 constexpr int kMaxSplits = 10;
-constexpr int kFusedAppendMax = 16;  // new window tokens per sequence appended inside the attention launch
+constexpr int kFusedAppendMax = 8;  // new window tokens per sequence appended inside the attention launch
 
 int attend_splits(int64_t bq) {
   int64_t s = (256 + bq - 1) / bq;
@@ -106,23 +106,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 
 __device__ __forceinline__ uint32_t h2_bits(v2h h) { return __builtin_bit_cast(uint32_t, h); }
 
+// A raw buffer of `bytes` bytes at p: a load past the end returns zeros without
+// a memory access, so a load that may not be wanted needs no branch around it
+// (the compiler waits for a load under a branch before the branch ends).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // 8 E2M1 codes (low nibble first) times a group scale, as four fp16x2 words
 __device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
   o[0] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
   o[1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
   o[2] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
   o[3] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
-}
-
-// 16 window channels of a new token: fp32 -> E4M3 bytes, as the window append stores them
-__device__ __forceinline__ uint4 encode16(const float* x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    const float4 v = *reinterpret_cast<const float4*>(x + 4 * k);
-    w[k] = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8) | (e4m3_encode(v.z) << 16) | (e4m3_encode(v.w) << 24);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
@@ -133,6 +129,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ float s_qmax[4][16];
   __shared__ float s_qfac[16];
   __shared__ int s_valid[kAttnTile];
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
 
   const int split = blockIdx.x;
   const int64_t bq = blockIdx.y;
@@ -149,57 +146,60 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   const int kg = tid & 7, grp = tid >> 3;  // keys 4kg..4kg+3, channels 16grp..16grp+15
   const int32_t* tk = a.topk + bq * 512 + 4 * kg;
 
-  // Raw bytes of a tile for this thread: main rows use w[i].x/.y (16 codes) and
-  // w[i].z (the scale byte); window rows use all 16 bytes.  Main-row loads are
-  // unconditional from a clamped row (masked through the scale) so that a tile's
-  // loads and the next tile's all stay in flight together.
+  // the tile's Top-K ids for this thread's four keys (-1 past the selected
+  // tiles); the load is unconditional, from a clamped tile
   auto load_idx = [&](int tile) -> int4 {
-    if (tile < t_end && tile * kAttnTile < 512) return *reinterpret_cast<const int4*>(tk + tile * kAttnTile);
-    return make_int4(-1, -1, -1, -1);
+    const int4 v = *reinterpret_cast<const int4*>(tk + min(tile, 512 / kAttnTile - 1) * kAttnTile);
+    return (tile < t_end && tile * kAttnTile < 512) ? v : make_int4(-1, -1, -1, -1);
   };
-  auto load_tile = [&](int tile, int4 e4, uint4* w, uint32_t& vmask) {
+  // Raw bytes of a tile for this thread, left as loaded until the tile is
+  // dequantised (arithmetic on them here would wait for the loads): w[i] is the
+  // aligned 16 bytes holding a main row's 16 codes of this thread (half grp & 1)
+  // or a window row's 16 bytes, sc[i] a main row's scale byte.  Both tile kinds
+  // issue the same loads, only their addresses differ, so no branch ends with a
+  // wait: a missing entry reads row 0 (masked through vmask), and a load a tile
+  // does not need (the scale of a window row, any row of an empty cache) reads
+  // this query's Top-K row instead.
+  const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.topk + bq * 512);
+  auto load_tile = [&](int tile, int4 e4, uint4* w, uint32_t* sc, uint32_t& vmask) {
+    const bool main_tile = tile * kAttnTile < 512;  // uniform: 512 is a multiple of the tile
+    const bool rows = main_tile && a.cap > 0;       // uniform
+    const int32_t es[4] = {e4.x, e4.y, e4.z, e4.w};
     vmask = 0;
-    if (tile * kAttnTile < 512) {  // uniform per tile: 512 is a multiple of the tile
-      if (a.cap > 0) {             // uniform; an empty cache has no row to stand in
-        const int32_t es[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const bool valid = es[i] >= 0;
-          vmask |= (uint32_t)valid << i;
-          const int64_t row = (int64_t)b * a.cap + (valid ? es[i] : 0);
-          const uint2 c = *reinterpret_cast<const uint2*>(a.kv_codes + row * 256 + 8 * grp);
-          w[i] = make_uint4(c.x, c.y, a.kv_scales[row * 32 + grp], 0u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);
-        const bool valid = pos >= 0;
-        vmask |= (uint32_t)valid << i;
-        if (pos >= new_lo && pos < new_hi) {
-          w[i] = encode16(a.swa_x + ((int64_t)b * a.swa_T + (pos - new_lo)) * 512 + 16 * grp);
-        } else {
-          w[i] = *reinterpret_cast<const uint4*>(a.swa + ((int64_t)b * a.S + (valid ? pos % a.S : 0)) * 512 + 16 * grp);
-        }
-      }
+    for (int i = 0; i < 4; i++) {
+      const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);  // window tiles
+      vmask |= (uint32_t)(main_tile ? es[i] >= 0 : pos >= 0) << i;
+      const int64_t row = (int64_t)b * a.cap + (es[i] >= 0 ? es[i] : 0);
+      const int32_t slot = main_tile ? 0 : (pos >= 0 ? pos : 0) % a.S;
+      const uint8_t* src = rows        ? a.kv_codes + row * 256 + 16 * (grp >> 1)
+                           : main_tile ? stand_in
+                                       : a.swa + ((int64_t)b * a.S + slot) * 512 + 16 * grp;
+      w[i] = *reinterpret_cast<const uint4*>(src);
+      sc[i] = *(rows ? a.kv_scales + row * 32 + grp : stand_in);
     }
   };
 
   uint4 wc[4] = {}, wn[4] = {};
+  uint32_t sc_c[4] = {}, sc_n[4] = {};
   uint32_t vc = 0, vn = 0;
   int4 ec = load_idx(t_begin);
   int4 en = load_idx(t_begin + 1);
 
-  // ---------------- fused window append: this workgroup's share of the new tokens
-  if (a.swa_x) {
-    const int rank = qi * a.splits + split, n_w = Q * a.splits;
-    for (int t = rank; t < a.swa_T; t += n_w) {
-      const int32_t pos = new_lo + t;
-      const float2 v = *reinterpret_cast<const float2*>(a.swa_x + ((int64_t)b * a.swa_T + t) * 512 + 2 * tid);
-      const uint32_t c = e4m3_encode(v.x) | (e4m3_encode(v.y) << 8);
-      *reinterpret_cast<uint16_t*>(a.swa + ((int64_t)b * a.S + pos % a.S) * 512 + 2 * tid) = (uint16_t)c;
-    }
+  // ---------------- new window tokens (fused append): the workgroups whose
+  // tiles reach the window load all of the sequence's new tokens (at most
+  // kFusedAppendMax), two channels per thread; they are encoded into s_new
+  // once the query is in, and these workgroups also write them to the ring
+  const int first_win = 512 / (a.tps * kAttnTile);  // first split holding window tiles
+  const bool has_win = t_end * kAttnTile > 512;
+  const bool stage = a.swa_x != nullptr && has_win;
+  float2 xv[kFusedAppendMax];
+  {
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(a.swa_x + (stage ? (int64_t)b * a.swa_T * 512 : 0), stage ? (uint32_t)a.swa_T * 2048u : 0u);
+#pragma unroll
+    for (int j = 0; j < kFusedAppendMax; j++)
+      xv[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(xr, (uint32_t)(j * 2048 + 8 * tid), 0, 0));
   }
 
   // ---------------- query: lane holds head lane%16, dims 128*wave + 32*kk + 8*(lane/16) .. +7
@@ -210,8 +210,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) qraw[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
     // the first two tiles' rows load while the query is scaled
-    load_tile(t_begin, ec, wc, vc);
-    if (t_begin + 1 < t_end) load_tile(t_begin + 1, en, wn, vn);
+    load_tile(t_begin, ec, wc, sc_c, vc);
+    load_tile(t_begin + 1, en, wn, sc_n, vn);  // past t_end: harmless loads, never used
     float qf[4][8];
     float amax = 0.0f;
 #pragma unroll
@@ -227,7 +227,21 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (lane < 16) s_qmax[wave][lane] = amax;
-    __syncthreads();
+    if (stage) {
+      // new token j: into s_new, and into the ring by the (query, window split)
+      // of rank j mod (Q * window splits)
+      const int n_w = Q * (a.splits - first_win), rank = qi * (a.splits - first_win) + (split - first_win);
+#pragma unroll
+      for (int j = 0; j < kFusedAppendMax; j++) {
+        if (j < a.swa_T) {
+          const uint16_t c = (uint16_t)(e4m3_encode(xv[j].x) | (e4m3_encode(xv[j].y) << 8));
+          reinterpret_cast<uint16_t*>(s_new + j * 512)[tid] = c;
+          if (j % n_w == rank)
+            reinterpret_cast<uint16_t*>(a.swa + ((int64_t)b * a.S + (new_lo + j) % a.S) * 512)[tid] = c;
+        }
+      }
+    }
+    lds_barrier();
     const int h = lane & 15;
     const float hmax = fmaxf(fmaxf(s_qmax[0][h], s_qmax[1][h]), fmaxf(s_qmax[2][h], s_qmax[3][h]));
     int ex;
@@ -248,31 +262,36 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   // DPP row and all hold the head's running max and sum)
   const int sm_h = tid >> 4;
   float m_run = -INFINITY, l_run = 0.0f;
-  __syncthreads();  // s_qfac is written
+  lds_barrier();  // s_qfac is written
   const float qfac = s_qfac[sm_h];
 
   for (int tile = t_begin; tile < t_end; tile++) {
     // prefetch the next tile's rows (the first workgroup tile's next came with
     // the query) and the indices of the one after
     const int4 e2 = load_idx(tile + 2);
-    if (tile > t_begin && tile + 1 < t_end) load_tile(tile + 1, en, wn, vn);
+    if (tile > t_begin && tile + 1 < t_end) load_tile(tile + 1, en, wn, sc_n, vn);
     // ---------------- dequantise this tile's keys into LDS (fp16, both layouts)
     {
       uint32_t hv[4][8];  // key i: channel pairs (2m, 2m+1) of the group, as fp16x2
       if (tile * kAttnTile < 512) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint32_t sc = ((vc >> i) & 1u) ? (wc[i].z & 0xFFu) : 0u;
+          const uint32_t sc = ((vc >> i) & 1u) ? (sc_c[i] & 0xFFu) : 0u;
           const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc * 0x0101u, 1.0f, false);
-          fp4_group(wc[i].x, s2, hv[i]);
-          fp4_group(wc[i].y, s2, hv[i] + 4);
+          // this thread's half of the 16 bytes, by mask (a select here is
+          // compiled as an index into the row, which moves wc to scratch)
+          const uint32_t odd = 0u - (uint32_t)(grp & 1);
+          fp4_group((wc[i].x & ~odd) | (wc[i].z & odd), s2, hv[i]);
+          fp4_group((wc[i].y & ~odd) | (wc[i].w & odd), s2, hv[i] + 4);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const bool valid = (vc >> i) & 1u;
-          const uint32_t xw[4] = {valid ? wc[i].x : 0u, valid ? wc[i].y : 0u, valid ? wc[i].z : 0u,
-                                  valid ? wc[i].w : 0u};
+          const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);
+          uint4 raw = wc[i];
+          if (pos >= new_lo && pos < new_hi) raw = *reinterpret_cast<const uint4*>(s_new + (pos - new_lo) * 512 + 16 * grp);
+          const uint32_t xw[4] = {valid ? raw.x : 0u, valid ? raw.y : 0u, valid ? raw.z : 0u, valid ? raw.w : 0u};
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             hv[i][2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
@@ -292,7 +311,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) s_valid[4 * kg + i] = (vc >> i) & 1u;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- partial S over this wave's 128 dims
 #pragma unroll
@@ -307,7 +326,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) s_red[wave][th][i][lane] = sacc[i];
     }
-    __syncthreads();
+    lds_barrier();
     // ---------------- scores (the four waves' partial sums) and online softmax:
     // thread (head h, keys 2j, 2j+1); partial element (th, i, lane) is head
     // 4*(lane/16)+i, key 16*th + lane%16
@@ -331,7 +350,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
       l_run = alpha * l_run + ps;
       if ((tid & 15) == 0) s_alpha[h] = alpha;
     }
-    __syncthreads();
+    lds_barrier();
     // ---------------- O = alpha * O + P V
     {
       const uint4 pa = *reinterpret_cast<const uint4*>(s_p + (lane & 15) * kPStride + 8 * (lane >> 4));
@@ -354,9 +373,12 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, vb, acc[ct], 0, 0, 0);
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 4; i++) wc[i] = wn[i];
+    for (int i = 0; i < 4; i++) {
+      wc[i] = wn[i];
+      sc_c[i] = sc_n[i];
+    }
     vc = vn;
     en = e2;
   }
@@ -366,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     s_m[sm_h] = m_run;
     s_l[sm_h] = l_run;
   }
-  __syncthreads();
+  lds_barrier();
   if (a.splits == 1) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {

@@ -110,6 +110,17 @@ __device__ __forceinline__ int wave_alloc(int count, int* counter) {
   return base + (int)incl - count;
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also makes
+// the thread's global stores visible to the workgroup, and on gfx9 that means
+// waiting for every global load, store and atomic the thread has in flight
+// (they all count in vmcnt), prefetches included; this barrier leaves them in
+// flight.  Use it where the threads exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup; `tmp` holds
 // one int per wave.  Returns the exclusive prefix, writes the total to *total.
 __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {

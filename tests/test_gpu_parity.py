@@ -331,6 +331,7 @@ def test_attend(csa, orc, B, Q, E, S, mode):
     (3, 1, 60, 128, 1),        # short sequences: the window reaches position 0
     (1, 64, 3000, 192, 64),    # a 64-token chunk appended by the workgroups of 64 queries
     (2, 2, 9000, 130, 2),      # two queries, ring barely above window + Q - 1
+    (2, 8, 4000, 136, 8),      # the most new tokens appended inside the attention launch
 ])
 def test_attend_fused_window_append(csa, orc, B, Q, E, S, T):
     """The fused append equals csa2_swa_append followed by attention: identical
