@@ -130,6 +130,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ float s_qfac[16];
   __shared__ int s_valid[kAttnTile];
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[512];                     // the query's Top-K row
 
   const int split = blockIdx.x;
   const int64_t bq = blockIdx.y;
@@ -146,11 +147,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   const int kg = tid & 7, grp = tid >> 3;  // keys 4kg..4kg+3, channels 16grp..16grp+15
   const int32_t* tk = a.topk + bq * 512 + 4 * kg;
 
-  // the tile's Top-K ids for this thread's four keys (-1 past the selected
-  // tiles); the load is unconditional, from a clamped tile
+  // the tile's Top-K ids for this thread's four keys, as loaded (from a clamped
+  // tile): load_tile decides whether they count, since any arithmetic on them
+  // here would wait for the load
   auto load_idx = [&](int tile) -> int4 {
-    const int4 v = *reinterpret_cast<const int4*>(tk + min(tile, 512 / kAttnTile - 1) * kAttnTile);
-    return (tile < t_end && tile * kAttnTile < 512) ? v : make_int4(-1, -1, -1, -1);
+    return *reinterpret_cast<const int4*>(tk + min(tile, 512 / kAttnTile - 1) * kAttnTile);
   };
   // Raw bytes of a tile for this thread, left as loaded until the tile is
   // dequantised (arithmetic on them here would wait for the loads): w[i] is the
@@ -158,13 +159,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   // or a window row's 16 bytes, sc[i] a main row's scale byte.  Both tile kinds
   // issue the same loads, only their addresses differ, so no branch ends with a
   // wait: a missing entry reads row 0 (masked through vmask), and a load a tile
-  // does not need (the scale of a window row, any row of an empty cache) reads
+  // does not need (the scale of a window row, any row of an empty cache, a tile past
+  // the split's) reads
   // this query's Top-K row instead.
   const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.topk + bq * 512);
   auto load_tile = [&](int tile, int4 e4, uint4* w, uint32_t* sc, uint32_t& vmask) {
+    const bool mine = tile < t_end;                 // uniform: tiles past the split hold nothing
     const bool main_tile = tile * kAttnTile < 512;  // uniform: 512 is a multiple of the tile
-    const bool rows = main_tile && a.cap > 0;       // uniform
-    const int32_t es[4] = {e4.x, e4.y, e4.z, e4.w};
+    const bool rows = main_tile && a.cap > 0 && mine;  // uniform
+    const int32_t es[4] = {mine ? e4.x : -1, mine ? e4.y : -1, mine ? e4.z : -1, mine ? e4.w : -1};
     vmask = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -172,9 +175,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
       vmask |= (uint32_t)(main_tile ? es[i] >= 0 : pos >= 0) << i;
       const int64_t row = (int64_t)b * a.cap + (es[i] >= 0 ? es[i] : 0);
       const int32_t slot = main_tile ? 0 : (pos >= 0 ? pos : 0) % a.S;
-      const uint8_t* src = rows        ? a.kv_codes + row * 256 + 16 * (grp >> 1)
-                           : main_tile ? stand_in
-                                       : a.swa + ((int64_t)b * a.S + slot) * 512 + 16 * grp;
+      const uint8_t* src = rows                ? a.kv_codes + row * 256 + 16 * (grp >> 1)
+                           : main_tile || !mine ? stand_in
+                                                : a.swa + ((int64_t)b * a.S + slot) * 512 + 16 * grp;
       w[i] = *reinterpret_cast<const uint4*>(src);
       sc[i] = *(rows ? a.kv_scales + row * 32 + grp : stand_in);
     }
@@ -185,6 +188,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   uint32_t vc = 0, vn = 0;
   int4 ec = load_idx(t_begin);
   int4 en = load_idx(t_begin + 1);
+  // the whole Top-K row, for the later tiles' ids (kept in LDS, so that the
+  // tile loop reads no ids from global memory)
+  const int2 idv = *reinterpret_cast<const int2*>(a.topk + bq * 512 + 2 * tid);
 
   // ---------------- new window tokens (fused append): the workgroups whose
   // tiles reach the window load all of the sequence's new tokens (at most
@@ -227,6 +233,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (lane < 16) s_qmax[wave][lane] = amax;
+    *reinterpret_cast<int2*>(s_ids + 2 * tid) = idv;
     if (stage) {
       // new token j: into s_new, and into the ring by the (query, window split)
       // of rank j mod (Q * window splits)
@@ -268,7 +275,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   for (int tile = t_begin; tile < t_end; tile++) {
     // prefetch the next tile's rows (the first workgroup tile's next came with
     // the query) and the indices of the one after
-    const int4 e2 = load_idx(tile + 2);
+    const int4 e2 = *reinterpret_cast<const int4*>(s_ids + min(tile + 2, 512 / kAttnTile - 1) * kAttnTile + 4 * kg);
     if (tile > t_begin && tile + 1 < t_end) load_tile(tile + 1, en, wn, sc_n, vn);
     // ---------------- dequantise this tile's keys into LDS (fp16, both layouts)
     {
