@@ -33,6 +33,7 @@ import synth  # noqa: E402
 METRIC = "CSA2 decode layer-steps/sec and achieved HBM GB/s (% of peak) at 128K ctx"
 UNIT = "layer-steps/s"
 PEAK_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 SM_SCALE = float(np.float32(1.0 / math.sqrt(512.0)))
 ROWS_PER_SEQ = 1 << 22          # row namespace of one sequence in the seeded generators
 FILL_FLOATS = 32 * 1024 * 1024  # fp32 values per cache-fill chunk
@@ -438,11 +439,23 @@ def main():
     idx_bytes = wl.B * wl.Q * E_idx * IDX_ROW if wl.decode else wl.B * E_idx * IDX_ROW
     achieved = idx_bytes / t_idx / 1e9
     traffic = traffic_from_profiles(wl, "index_full")
-    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
-                frac=round(achieved / PEAK_GBPS, 4), traffic=traffic,
-                kernel="index_score + index_filter + index_final (one csa2_index_score_topk Full call)",
-                bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
-    log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
+    kernel_name = "index_score + index_filter + index_final (one csa2_index_score_topk Full call)"
+    if wl.decode:
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBPS, 4), traffic=traffic, kernel=kernel_name,
+                    bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
+        log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
+    else:
+        # a prefill chunk scores every query against every entry it sees: a dense
+        # contraction on the bf16 matrix cores, 2 x 4 heads x 64 dims per pair
+        pos = wl.ctx - wl.Q + np.arange(wl.Q)
+        pairs = int(np.minimum(E_idx, (pos + 1) // wl.r).sum()) * wl.B
+        flops = 2 * 4 * 64 * pairs
+        tflops = flops / t_idx / 1e12
+        roof = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=kernel_name,
+                    flops_per_launch=flops, avg_launch_us=round(t_idx * 1e6, 2))
+        log(f"Full indexer call: {t_idx * 1e6:.1f} us, {tflops:.1f} TFLOP/s on {flops / 1e9:.2f} GFLOP")
 
     if args.copy_calibration:
         copy_calibration()

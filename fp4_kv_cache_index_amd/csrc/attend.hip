@@ -121,6 +121,7 @@ __device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
   o[3] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
 }
 
+template <bool kRefill>
 __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[kAttnTile * kKStride];
   __shared__ float s_red[4][2][4][kRedStride];  // [wave][key block][row group i][lane]
@@ -272,31 +273,33 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   lds_barrier();  // s_qfac is written
   const float qfac = s_qfac[sm_h];
 
-  for (int tile = t_begin; tile < t_end; tile++) {
-    // prefetch the next tile's rows (the first workgroup tile's next came with
-    // the query) and the indices of the one after
-    const int4 e2 = *reinterpret_cast<const int4*>(s_ids + min(tile + 2, 512 / kAttnTile - 1) * kAttnTile + 4 * kg);
-    if (tile > t_begin && tile + 1 < t_end) load_tile(tile + 1, en, wn, sc_n, vn);
-    // ---------------- dequantise this tile's keys into LDS (fp16, both layouts)
+  // One tile: dequantise the rows held in (w, sc, vm) into LDS, refill those
+  // registers with the tile two ahead (kRefill: so a tile's rows are in flight
+  // while the two before it are processed; past the split they read a
+  // stand-in), then S, the online softmax and O += PV.  Tiles alternate between
+  // two register sets, and no load is under a branch.  Splits of at most two
+  // tiles load both at entry and need no refill.
+  auto tile_step = [&](int tile, uint4(&w)[4], uint32_t(&sc)[4], uint32_t& vm) {
+    // ---------------- dequantise this tile's keys into LDS (fp16 [key][dim])
     {
       uint32_t hv[4][8];  // key i: channel pairs (2m, 2m+1) of the group, as fp16x2
       if (tile * kAttnTile < 512) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint32_t sc = ((vc >> i) & 1u) ? (sc_c[i] & 0xFFu) : 0u;
-          const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc * 0x0101u, 1.0f, false);
+          const uint32_t sb = ((vm >> i) & 1u) ? (sc[i] & 0xFFu) : 0u;
+          const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb * 0x0101u, 1.0f, false);
           // this thread's half of the 16 bytes, by mask (a select here is
-          // compiled as an index into the row, which moves wc to scratch)
+          // compiled as an index into the row, which moves the rows to scratch)
           const uint32_t odd = 0u - (uint32_t)(grp & 1);
-          fp4_group((wc[i].x & ~odd) | (wc[i].z & odd), s2, hv[i]);
-          fp4_group((wc[i].y & ~odd) | (wc[i].w & odd), s2, hv[i] + 4);
+          fp4_group((w[i].x & ~odd) | (w[i].z & odd), s2, hv[i]);
+          fp4_group((w[i].y & ~odd) | (w[i].w & odd), s2, hv[i] + 4);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const bool valid = (vc >> i) & 1u;
+          const bool valid = (vm >> i) & 1u;
           const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);
-          uint4 raw = wc[i];
+          uint4 raw = w[i];
           if (pos >= new_lo && pos < new_hi) raw = *reinterpret_cast<const uint4*>(s_new + (pos - new_lo) * 512 + 16 * grp);
           const uint32_t xw[4] = {valid ? raw.x : 0u, valid ? raw.y : 0u, valid ? raw.z : 0u, valid ? raw.w : 0u};
 #pragma unroll
@@ -316,7 +319,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     }
     if (grp == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) s_valid[4 * kg + i] = (vc >> i) & 1u;
+      for (int i = 0; i < 4; i++) s_valid[4 * kg + i] = (vm >> i) & 1u;
+    }
+    if constexpr (kRefill) {
+      const int4 e = *reinterpret_cast<const int4*>(s_ids + min(tile + 2, 512 / kAttnTile - 1) * kAttnTile + 4 * kg);
+      load_tile(tile + 2, e, w, sc, vm);
     }
     lds_barrier();
 
@@ -381,14 +388,13 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
       }
     }
     lds_barrier();
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      wc[i] = wn[i];
-      sc_c[i] = sc_n[i];
-    }
-    vc = vn;
-    en = e2;
+  };
+  int tile = t_begin;
+  for (; tile + 1 < t_end; tile += 2) {
+    tile_step(tile, wc, sc_c, vc);
+    tile_step(tile + 1, wn, sc_n, vn);
   }
+  if (tile < t_end) tile_step(tile, wc, sc_c, vc);
 
   // ---------------- epilogue: rows 4*(lane/16)+i are heads, column lane%16 a dim
   if ((tid & 15) == 0) {
@@ -507,7 +513,10 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
     a.part_o = (float*)base;
     a.part_ml = a.part_o + (int64_t)a.splits * bq * 16 * 512;
   }
-  hipLaunchKernelGGL(attend_kernel, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
+  if (a.tps > 2)
+    hipLaunchKernelGGL(attend_kernel<true>, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attend_kernel<false>, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq, 16), dim3(kThreads), 0, stream, a.part_o, a.part_ml,
