@@ -68,11 +68,12 @@ int attend_splits(int64_t bq) {
 
 static inline int tiles_per_split(int splits) { return (kTilesPerQuery + splits - 1) / splits; }
 
-// [partial O: splits x bq x 16 x 512 f32][partial (max, sum): splits x bq x 16 x 2 f32]
+// [partial O, normalised by its own sum: splits x bq x 16 x 512 fp16]
+// [partial (max, sum): splits x bq x 16 x 2 f32]
 size_t attend_ws_bytes(int64_t bq) {
   const int s = attend_splits(bq);
   if (s == 1) return 0;
-  return 256 + (size_t)s * bq * (16 * 512 * 4 + 16 * 2 * 4);
+  return 256 + (size_t)s * bq * (16 * 512 * 2 + 16 * 2 * 4);
 }
 
 struct AttnArgs {
@@ -93,7 +94,7 @@ struct AttnArgs {
   int32_t tps, splits;
   uint16_t* out;
   float* lse;
-  float* part_o;
+  _Float16* part_o;
   float* part_ml;
   int64_t bq_total;
 };
@@ -418,12 +419,16 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     return;
   }
   {
-    float* po = a.part_o + ((int64_t)split * a.bq_total + bq) * 16 * 512;
+    // the split's output normalised by its own sum: |value| <= the largest key
+    // value (2688), so fp16 holds it to 2^-12 relative
+    _Float16* po = a.part_o + ((int64_t)split * a.bq_total + bq) * 16 * 512;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int h = 4 * (lane >> 4) + i;
+      const float l = s_l[h];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-      for (int ct = 0; ct < 8; ct++) po[h * 512 + 128 * wave + 16 * ct + (lane & 15)] = acc[ct][i];
+      for (int ct = 0; ct < 8; ct++) po[h * 512 + 128 * wave + 16 * ct + (lane & 15)] = (_Float16)(acc[ct][i] * inv);
     }
     if (tid < 16) {
       float* pm = a.part_ml + ((int64_t)split * a.bq_total + bq) * 32;
@@ -433,24 +438,25 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   }
 }
 
-// One workgroup per (query, head): combine the splits' unnormalised partials by
-// their log-sum-exp weights; each thread owns two of the 512 output channels.
+// One workgroup per (query, head): combine the splits' normalised partials,
+// each weighted by its sum times exp(its max - the overall max); each thread
+// owns two of the 512 output channels.
 __global__ void __launch_bounds__(kThreads)
-    attend_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
+    attend_merge_kernel(const _Float16* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
                         int64_t bq_total, uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int64_t bq = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   // every load is issued from a clamped split so they all stay in flight together
   float ms[kMaxSplits], ls[kMaxSplits];
-  float2 v[kMaxSplits];
+  v2h v[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; s++) {
     const int sc = min(s, splits - 1);
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((int64_t)sc * bq_total + bq) * 32 + 2 * h);
     ms[s] = ml.x;
     ls[s] = ml.y;
-    v[s] = *reinterpret_cast<const float2*>(part_o + (((int64_t)sc * bq_total + bq) * 16 + h) * 512 + 2 * tid);
+    v[s] = *reinterpret_cast<const v2h*>(part_o + (((int64_t)sc * bq_total + bq) * 16 + h) * 512 + 2 * tid);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -459,10 +465,10 @@ __global__ void __launch_bounds__(kThreads)
   float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; s++) {
-    const float w = (s < splits && ms[s] != -INFINITY) ? __expf(ms[s] - M) : 0.0f;
-    L += w * ls[s];
-    o0 += w * v[s].x;
-    o1 += w * v[s].y;
+    const float w = (s < splits && ms[s] != -INFINITY) ? __expf(ms[s] - M) * ls[s] : 0.0f;
+    L += w;
+    o0 += w * (float)v[s][0];
+    o1 += w * (float)v[s][1];
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const uint32_t packed = (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16);
@@ -510,8 +516,8 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
   a.bq_total = bq;
   if (a.splits > 1) {
     uint8_t* base = (uint8_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-    a.part_o = (float*)base;
-    a.part_ml = a.part_o + (int64_t)a.splits * bq * 16 * 512;
+    a.part_o = (_Float16*)base;
+    a.part_ml = (float*)(a.part_o + (int64_t)a.splits * bq * 16 * 512);
   }
   if (a.tps > 2)
     hipLaunchKernelGGL(attend_kernel<true>, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
