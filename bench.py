@@ -452,21 +452,28 @@ def main():
     durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
     t_idx = float(np.mean(durs))
     E_idx = int(wl.caches[0].length.max().item()) if wl.decode else wl.ctx // wl.r
-    idx_bytes = wl.B * wl.Q * E_idx * IDX_ROW if wl.decode else wl.B * E_idx * IDX_ROW
-    achieved = idx_bytes / t_idx / 1e9
+    # bytes: every indexer key of the batch once (the queries of a sequence share them);
+    # FLOPs: 2 x 4 heads x 64 dims per (query, visible entry) pair
+    idx_bytes = wl.B * E_idx * IDX_ROW
+    if wl.decode:
+        pairs = wl.B * E_idx
+    else:
+        pos = wl.ctx - wl.Q + np.arange(wl.Q)
+        pairs = int(np.minimum(E_idx, (pos + 1) // wl.r).sum()) * wl.B
+    flops = 2 * 4 * 64 * pairs
     traffic = traffic_from_profiles(wl, "index_full")
     kernel_name = "index_score + index_filter + index_final (one csa2_index_score_topk Full call)"
-    if wl.decode:
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_GBPS * 1e9)  # FLOP per byte where the bf16 matrix cores take over
+    if flops / idx_bytes < ridge:
+        # decode (one or a few queries per sequence): bound by streaming the indexer keys
+        achieved = idx_bytes / t_idx / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_GBPS, 4), traffic=traffic, kernel=kernel_name,
                     bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
         log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
     else:
         # a prefill chunk scores every query against every entry it sees: a dense
-        # contraction on the bf16 matrix cores, 2 x 4 heads x 64 dims per pair
-        pos = wl.ctx - wl.Q + np.arange(wl.Q)
-        pairs = int(np.minimum(E_idx, (pos + 1) // wl.r).sum()) * wl.B
-        flops = 2 * 4 * 64 * pairs
+        # contraction on the bf16 matrix cores
         tflops = flops / t_idx / 1e12
         roof = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=kernel_name,

@@ -58,8 +58,15 @@ constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
 constexpr int kMaxSplits = 10;
 constexpr int kFusedAppendMax = 8;  // new window tokens per sequence appended inside the attention launch
 
+// Splits per query, at most kMaxSplits, rounded so every split holds as many
+// tiles.  At most one workgroup per compute unit while that still gives four
+// or more splits: workgroups sharing a compute unit mostly queue behind each
+// other (measured: 32 queries run best as 7 splits, not 10).  Fewer queries
+// than that get about two workgroups per compute unit instead (96 queries: 5
+// splits beat 2, 3 and 10).
 int attend_splits(int64_t bq) {
-  int64_t s = (256 + bq - 1) / bq;
+  int64_t s = 256 / bq;
+  if (s < 4) s = (512 + bq - 1) / bq;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
   const int tps = (int)((kTilesPerQuery + s - 1) / s);

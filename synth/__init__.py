@@ -28,6 +28,10 @@ WORKLOADS = {
             group=("full", "reuse", "reuse", "reuse", "reuse", "reuse")),
     4: dict(name="f_ri_2ru_b4_ctx1m", B=4, ctx=1048576, ratio=1, Q=1,
             group=("full_pool", "reindex", "reuse", "reuse")),
+    # multi-token decode: the next token plus 5 draft tokens per sequence, each
+    # query causal over the entries up to its own position
+    5: dict(name="mtp_q6_f_ri_2ru_b16_ctx128k", B=16, ctx=131072, ratio=1, Q=6,
+            group=("full_pool", "reindex", "reuse", "reuse")),
 }
 
 

@@ -24,6 +24,7 @@ CASES = {
     2: (2, None),
     3: (1, [0, 1, 2, 511, 1024, 1500, 2046, 2047]),
     4: (1, None),
+    5: (2, None),
 }
 
 
@@ -36,7 +37,7 @@ def gpu():
     return csa
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5])
 def test_full_size_step(gpu, cid):
     hs, qsel = CASES[cid]
     print(f"config {cid}: building workload", flush=True)
@@ -68,10 +69,14 @@ def test_full_size_step(gpu, cid):
                     swaps += topk_swaps(g_topk[b, j], r["topk"][b, j], r["scores"][b, j], name=f"L{l} b{b} q{qs[j]}")
             if mode == "full_pool":
                 g_pool = wl.pool[:hs].cpu().numpy()[:, qs]
+                q_pos = ost.q_pos
                 for b in range(hs):
-                    n_vis = int(ost.oc.length[b])
-                    swaps += pool_block_swaps(g_pool[b, 0], r["pool"][b, 0], r["scores"][b, 0], n_vis,
-                                              name=f"pool b{b}")
+                    for j in range(len(qs)):
+                        # entries visible to this query (all of them at single-token decode)
+                        n_vis = int(ost.oc.length[b]) if q_pos is None else min(int(ost.oc.length[b]),
+                                                                                (int(q_pos[b, j]) + 1) // wl.r)
+                        swaps += pool_block_swaps(g_pool[b, j], r["pool"][b, j], r["scores"][b, j], n_vis,
+                                                  name=f"pool b{b} q{qs[j]}")
         g_out = wl.out[l][:hs].float().cpu().numpy()[:, qs]
         g_used = wl.topk[topk_layer][:hs].cpu().numpy()[:, qs]
         for b in range(hs):
