@@ -121,6 +121,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// Workgroup order aware of the 8 XCDs: the dispatcher deals workgroups to the
+// XCDs round-robin (workgroup L to XCD L mod 8), and each XCD has its own L2.
+// Rank r = (L mod 8) * (n / 8) + L / 8 gives XCD x the consecutive ranks
+// [x n/8, (x+1) n/8), so the workgroups of one query (its splits, or its
+// heads in the merge) share an XCD and its L2 (the query, the Top-K ids, the
+// split partials).  Identity when n is not a multiple of 8.
+__device__ __forceinline__ int64_t xcd_rank(int64_t L, int64_t n) {
+  return (n & 7) == 0 ? (L & 7) * (n >> 3) + (L >> 3) : L;
+}
+
 // 8 E2M1 codes (low nibble first) times a group scale, as four fp16x2 words
 __device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
   o[0] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
@@ -141,8 +151,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
   __shared__ __attribute__((aligned(16))) int32_t s_ids[512];                     // the query's Top-K row
 
-  const int split = blockIdx.x;
-  const int64_t bq = blockIdx.y;
+  const int64_t wr = xcd_rank(blockIdx.x, (int64_t)a.splits * a.bq_total);
+  const int split = (int)(wr % a.splits);
+  const int64_t bq = wr / a.splits;
   const int Q = a.Q;
   const int b = (int)(bq / Q), qi = (int)(bq % Q);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -451,8 +462,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
 __global__ void __launch_bounds__(kThreads)
     attend_merge_kernel(const _Float16* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
                         int64_t bq_total, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int64_t bq = blockIdx.x;
-  const int h = blockIdx.y;
+  const int64_t wr = xcd_rank(blockIdx.x, bq_total * 16);  // the XCD of the query's attention splits
+  const int64_t bq = wr >> 4;
+  const int h = (int)(wr & 15);
   const int tid = threadIdx.x;
   // every load is issued from a clamped split so they all stay in flight together
   float ms[kMaxSplits], ls[kMaxSplits];
@@ -526,13 +538,14 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
     a.part_o = (_Float16*)base;
     a.part_ml = (float*)(a.part_o + (int64_t)a.splits * bq * 16 * 512);
   }
+  const unsigned n_wg = (unsigned)(a.splits * bq);  // (split, query) pairs in XCD-aware order
   if (a.tps > 2)
-    hipLaunchKernelGGL(attend_kernel<true>, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attend_kernel<true>, dim3(n_wg), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attend_kernel<false>, dim3(a.splits, (unsigned)bq), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attend_kernel<false>, dim3(n_wg), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)bq, 16), dim3(kThreads), 0, stream, a.part_o, a.part_ml,
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(bq * 16)), dim3(kThreads), 0, stream, a.part_o, a.part_ml,
                      a.splits, bq, out, lse);
   return hipGetLastError();
 }
