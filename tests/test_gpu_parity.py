@@ -162,12 +162,14 @@ def test_index_full_topk_and_pool(csa, orc, E):
     print(f"E={E}: boundary swaps {swaps}")
 
 
-def test_index_full_multiquery_causal_ratio2(csa, orc):
+@pytest.mark.parametrize("nq", [4, 9])  # one group of four queries per workgroup / groups of eight, ragged
+def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
     B, E, ratio = 2, 5000, 2
     cap = 5003
     oc = oracle_cache_ik(orc, B, cap, [E, 3001], 21, ratio=ratio)
     q_pos = np.array([[0, 1, 2, 3, 1023, 1024, 4095, 9999, 10005],
                       [5, 6, 600, 601, 2047, 6001, 6002, 6003, 100]], np.int32)
+    q_pos = np.ascontiguousarray(q_pos[:, -nq:])
     Q = q_pos.shape[1]
     iq = synth.normal(21, "iq", (B, Q, 4, 64))
     ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_pool=True, want_scores=True)
