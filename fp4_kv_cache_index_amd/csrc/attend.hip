@@ -121,16 +121,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Workgroup order aware of the 8 XCDs: the dispatcher deals workgroups to the
-// XCDs round-robin (workgroup L to XCD L mod 8), and each XCD has its own L2.
-// Rank r = (L mod 8) * (n / 8) + L / 8 gives XCD x the consecutive ranks
-// [x n/8, (x+1) n/8), so the workgroups of one query (its splits, or its
-// heads in the merge) share an XCD and its L2 (the query, the Top-K ids, the
-// split partials).  Identity when n is not a multiple of 8.
-__device__ __forceinline__ int64_t xcd_rank(int64_t L, int64_t n) {
-  return (n & 7) == 0 ? (L & 7) * (n >> 3) + (L >> 3) : L;
-}
-
 // 8 E2M1 codes (low nibble first) times a group scale, as four fp16x2 words
 __device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
   o[0] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
