@@ -182,7 +182,9 @@ def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
             pool_block_swaps(pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
 
 
-@pytest.mark.parametrize("E", [9000, 40000])  # selection inside the final kernel / through the filter kernel
+# selection inside the final kernel / entries through the filter kernel / 8,750 tied pool blocks, more
+# than the candidate buffer holds, selected inside the final kernel
+@pytest.mark.parametrize("E", [9000, 40000, 70000])
 def test_index_relu_zero_ties_exact(csa, orc, E):
     """Every score is 0: all keys tie, more than the candidate buffer holds, so
     the exact fallback that streams the keys decides by entry index."""
