@@ -249,10 +249,247 @@ class OracleStep:
         return res
 
 
+# The whole 38-layer CSA2 schedule of one decode token: three encoder groups of
+# Full + 5 Reuse, each Full layer owning a ratio-2 cache, then the decoder's
+# Full (+pool) + 3 Reuse and four groups of Reindex + 3 Reuse over the decoder's
+# ratio-1 cache (technologiesdigest "CSA2"; ai.info "Methodology").
+SCHEDULE38 = ([("full", "enc0")] + [("reuse", "enc0")] * 5 + [("full", "enc1")] + [("reuse", "enc1")] * 5 +
+              [("full", "enc2")] + [("reuse", "enc2")] * 5 + [("full_pool", "dec")] + [("reuse", "dec")] * 3 +
+              ([("reindex", "dec")] + [("reuse", "dec")] * 3) * 4)
+ENC_CACHES = ("enc0", "enc1", "enc2")
+
+
+class Schedule38:
+    """Device state of the 38-layer schedule over B sequences of `ctx` tokens.
+
+    A step is two decode tokens, at positions ctx and ctx + 1.  An encoder
+    entry summarises two tokens, so the first token leaves it pending (the
+    encoder layers see ctx / 2 entries) and the second completes it: each
+    encoder Full layer appends the pair's entry before scoring.  The decoder
+    appends one entry per token.  Every step first resets the lengths, so each
+    step sees the same context.  76 layer-steps per step."""
+
+    def __init__(self, cid, B, ctx, replicas, keep_host_seqs=0):
+        import fp4_kv_cache_index_amd as csa
+        assert ctx % 2 == 0
+        self.csa, self.cid, self.B, self.ctx = csa, cid, B, ctx
+        w = synth.WORKLOADS.get(cid, {})
+        self.name = w["name"] if (w.get("B"), w.get("ctx")) == (B, ctx) else f"sched38_b{B}_ctx{ctx}"
+        self.r, self.Q, self.decode, self.tokens = 1, 1, False, 2
+        self.group = [m for m, _ in SCHEDULE38]
+        self.L = len(SCHEDULE38) * self.tokens
+        self.S = 128
+        self.E0 = {"dec": ctx}
+        self.E0.update({n: ctx // 2 for n in ENC_CACHES})
+        self.ratio = {"dec": 1}
+        self.ratio.update({n: 2 for n in ENC_CACHES})
+        dev = "cuda"
+        t0 = time.time()
+        self.caches = [{n: csa.Cache(B, self.E0[n] + 8, self.ratio[n]) for n in self.E0} for _ in range(replicas)]
+        hs = min(keep_host_seqs, B)
+        self.host_rows = {} if hs else None
+        T_fill = max(2, (FILL_FLOATS // (B * 512)) // 2 * 2)
+        for n, c in self.caches[0].items():
+            r = self.ratio[n]
+            if hs:
+                self.host_rows[n] = dict(kv=np.empty((hs, ctx, 512), np.float32),
+                                         ik=np.empty((hs, ctx // r, 64), np.float32),
+                                         lg=np.empty((hs, ctx, 512), np.float32) if r == 2 else None)
+            tok = 0
+            while tok < ctx:
+                T = min(T_fill, ctx - tok)
+                kv = torch.stack([synth.torch_normal_rows(cid, f"kv_{n}", b * ROWS_PER_SEQ + tok, T, 512)
+                                  for b in range(B)])
+                ik = torch.stack([synth.torch_normal_rows(cid, f"ik_{n}", b * ROWS_PER_SEQ + tok // r, T // r, 64)
+                                  for b in range(B)])
+                lg = (torch.stack([synth.torch_normal_rows(cid, f"lg_{n}", b * ROWS_PER_SEQ + tok, T, 512)
+                                   for b in range(B)]) if r == 2 else None)
+                csa.quantize_append(c, kv, ik, logits=lg)
+                if hs:
+                    h = self.host_rows[n]
+                    h["kv"][:, tok:tok + T] = kv[:hs].cpu().numpy()
+                    h["ik"][:, tok // r:(tok + T) // r] = ik[:hs].cpu().numpy()
+                    if r == 2:
+                        h["lg"][:, tok:tok + T] = lg[:hs].cpu().numpy()
+                tok += T
+        torch.cuda.synchronize()
+        for rep in self.caches[1:]:
+            for n, c in rep.items():
+                for f in ("kv_codes", "kv_scales", "ik_codes", "ik_scales", "length"):
+                    getattr(c, f).copy_(getattr(self.caches[0][n], f))
+        for rep in self.caches:
+            for n, c in rep.items():
+                c.host_len_bound = self.E0[n]
+        log(f"filled {replicas} replica(s) of 3 encoder caches ({ctx // 2} entries) and a decoder cache "
+            f"({ctx} entries) x {B} sequences in {time.time() - t0:.1f}s")
+        # per-layer windows: the 128 tokens before the step
+        nL = len(SCHEDULE38)
+        self.swa_rows = [torch.stack([synth.torch_normal_rows(cid, f"swa{l}", b * ROWS_PER_SEQ + ctx - 128, 128, 512)
+                                      for b in range(B)]) for l in range(nL)]
+        seq_before = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+        self.swas = []
+        for _ in range(replicas):
+            per = []
+            for l in range(nL):
+                sw = torch.zeros((B, self.S, 512), dtype=torch.uint8, device=dev)
+                csa.swa_append(sw, self.swa_rows[l], seq_before)
+                per.append(sw)
+            self.swas.append(per)
+        # step inputs (one set per replica), token t at position ctx + t
+        self.q_pos = [torch.full((B, 1), ctx + t, dtype=torch.int32, device=dev) for t in range(2)]
+        self.seq = [torch.full((B,), ctx + t + 1, dtype=torch.int32, device=dev) for t in range(2)]
+        rows = lambda tag, n, w: torch.stack([synth.torch_normal_rows(cid, tag, b * ROWS_PER_SEQ, n, w)
+                                              for b in range(B)])
+        self.inputs = []
+        for i in range(replicas):
+            g = f"s38step{i}"
+            inp = dict(
+                # encoder pair (2 tokens -> 1 entry) appended at the second token
+                enc={n: dict(kv=rows(g + "kv" + n, 2, 512), lg=rows(g + "lg" + n, 2, 512), ik=rows(g + "ik" + n, 1, 64))
+                     for n in ENC_CACHES},
+                dec=[dict(kv=rows(g + f"kvdec{t}", 1, 512), ik=rows(g + f"ikdec{t}", 1, 64)) for t in range(2)],
+                x=[[rows(g + f"x{t}_{l}", 1, 512) for l in range(nL)] for t in range(2)],
+                iq=[[(rows(g + f"iq{t}_{l}", 4, 64).reshape(B, 1, 4, 64).contiguous()
+                      if SCHEDULE38[l][0] != "reuse" else None) for l in range(nL)] for t in range(2)],
+                q=[[rows(g + f"q{t}_{l}", 16, 512).reshape(B, 1, 16, 512).to(torch.bfloat16).contiguous()
+                    for l in range(nL)] for t in range(2)],
+            )
+            self.inputs.append(inp)
+        self.topk = {n: torch.empty((B, 1, 512), dtype=torch.int32, device=dev) for n in ("enc", "dec_full", "dec_ri")}
+        self.pool = torch.empty((B, 1, csa.POOL), dtype=torch.int32, device=dev)
+        self.out = [[torch.empty((B, 1, 16, 512), dtype=torch.bfloat16, device=dev) for _ in range(nL)]
+                    for _ in range(2)]
+        capmax = max(c.capacity for c in self.caches[0].values())
+        self.ws_idx = torch.zeros(max(1, csa.workspace_bytes(csa.OP_INDEX, B, 1, capmax)), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_att = torch.zeros(max(1, csa.workspace_bytes(csa.OP_ATTEND, B, 1, capmax)), dtype=torch.uint8,
+                                  device=dev)
+        # the topk every layer attends with, per token (filled by step(); the test reads it)
+        self.used = [[None] * nL for _ in range(2)]
+        self.used_pool = [None, None]
+        torch.cuda.synchronize()
+
+    def step(self, i, record=False):
+        """One step on replica i; with `record` (eager runs only) keep a copy of
+        the Top-K (and pool) each layer attended with in self.used / self.used_pool."""
+        csa = self.csa
+        cs, inp, swas = self.caches[i], self.inputs[i], self.swas[i]
+        for n, c in cs.items():
+            c.length.fill_(self.E0[n])
+            c.host_len_bound = self.E0[n]
+        for t in range(2):
+            if t == 1:
+                for n in ENC_CACHES:
+                    e = inp["enc"][n]
+                    csa.quantize_append(cs[n], e["kv"], e["ik"], logits=e["lg"])
+            csa.quantize_append(cs["dec"], inp["dec"][t]["kv"], inp["dec"][t]["ik"])
+            topk = None
+            for l, (mode, cn) in enumerate(SCHEDULE38):
+                c = cs[cn]
+                if mode == "full":
+                    topk = self.topk["enc"]
+                    csa.index_score_topk(c, csa.FULL, inp["iq"][t][l], topk, q_pos=self.q_pos[t], ws=self.ws_idx)
+                elif mode == "full_pool":
+                    topk = self.topk["dec_full"]
+                    csa.index_score_topk(c, csa.FULL, inp["iq"][t][l], topk, q_pos=self.q_pos[t],
+                                         pool_out=self.pool, ws=self.ws_idx)
+                elif mode == "reindex":
+                    topk = self.topk["dec_ri"]
+                    csa.index_score_topk(c, csa.REINDEX, inp["iq"][t][l], topk, q_pos=self.q_pos[t],
+                                         pool_in=self.pool, ws=self.ws_idx)
+                if record:
+                    if mode != "reuse":
+                        snap = topk.clone()
+                        if mode == "full_pool":
+                            self.used_pool[t] = self.pool.clone()
+                    self.used[t][l] = snap
+                csa.sparse_attend(c, topk, swas[l], inp["q"][t][l], self.out[t][l], SM_SCALE, q_pos=self.q_pos[t],
+                                  ws=self.ws_att, swa_x=inp["x"][t][l], swa_len=self.seq[t])
+
+    def full_index(self, i):
+        """The decoder's Full call (with the pool) on the step's second token."""
+        self.csa.index_score_topk(self.caches[i]["dec"], self.csa.FULL, self.inputs[i]["iq"][1][18],
+                                  self.topk["dec_full"], q_pos=self.q_pos[1], pool_out=self.pool, ws=self.ws_idx)
+
+    def index_bytes(self):
+        return self.B * (self.ctx + 2) * IDX_ROW
+
+    def step_bytes(self, E=None):
+        """Algorithmic KV + indexer bytes of one step (two tokens)."""
+        B, by = self.B, 0
+        for t in range(2):
+            e_enc = self.ctx // 2 + t
+            by += 3 * B * e_enc * IDX_ROW               # encoder Full scans
+            by += B * (self.ctx + t + 1) * IDX_ROW       # decoder Full scan
+            by += 4 * B * min(16384, self.ctx + t + 1) * IDX_ROW  # Reindex pools
+            by += len(SCHEDULE38) * B * 512 * MAIN_ROW   # gathers
+            by += len(SCHEDULE38) * B * 128 * SWA_ROW    # windows
+        return by
+
+
+class OracleSchedule38:
+    """The oracle's replay of Schedule38's step on its first sequences, from the
+    same seeded rows and step inputs (host copies)."""
+
+    def __init__(self, wl):
+        import oracle as orc
+        self.orc, self.wl = orc, wl
+        hs = next(iter(wl.host_rows.values()))["kv"].shape[0]
+        self.hs = hs
+        self.oc = {}
+        for n, h in wl.host_rows.items():
+            c = orc.Cache(hs, wl.caches[0][n].capacity, wl.ratio[n])
+            orc.quantize_append(c, h["kv"], h["ik"], logits=h["lg"])
+            self.oc[n] = c
+        self.swas = []
+        for l in range(len(SCHEDULE38)):
+            sw = np.zeros((hs, wl.S, 512), np.uint8)
+            orc.swa_append(sw, wl.swa_rows[l][:hs].cpu().numpy(), np.full(hs, wl.ctx, np.int32))
+            self.swas.append(sw)
+        h = lambda x: None if x is None else x[:hs].float().cpu().numpy()
+        inp = wl.inputs[0]
+        self.inp = dict(enc={n: {k: h(v) for k, v in e.items()} for n, e in inp["enc"].items()},
+                        dec=[{k: h(v) for k, v in d.items()} for d in inp["dec"]],
+                        x=[[h(x) for x in xs] for xs in inp["x"]],
+                        iq=[[h(x) for x in xs] for xs in inp["iq"]],
+                        q=[[h(x) for x in xs] for xs in inp["q"]])
+        self.q_pos = [np.full((hs, 1), wl.ctx + t, np.int32) for t in range(2)]
+
+    def step(self, want_scores=False):
+        """Returns res[t][l] = dict(topk, pool, scores, out) for token t and layer l."""
+        orc, wl, oc, inp = self.orc, self.wl, self.oc, self.inp
+        for n, c in oc.items():
+            c.length[:] = wl.E0[n]
+        res = [[None] * len(SCHEDULE38) for _ in range(2)]
+        for t in range(2):
+            if t == 1:
+                for n in ENC_CACHES:
+                    e = inp["enc"][n]
+                    orc.quantize_append(oc[n], e["kv"], e["ik"], logits=e["lg"])
+            orc.quantize_append(oc["dec"], inp["dec"][t]["kv"], inp["dec"][t]["ik"])
+            seq = np.full(self.hs, wl.ctx + t + 1, np.int32)
+            topk, pool = None, None
+            for l, (mode, cn) in enumerate(SCHEDULE38):
+                c = oc[cn]
+                orc.swa_append(self.swas[l], inp["x"][t][l], seq)
+                scores, lpool = None, None
+                if mode in ("full", "full_pool"):
+                    topk, lpool, scores = orc.index_topk(c, orc.FULL, inp["iq"][t][l], q_pos=self.q_pos[t],
+                                                         want_pool=mode == "full_pool", want_scores=want_scores)
+                    if mode == "full_pool":
+                        pool = lpool
+                elif mode == "reindex":
+                    topk, _, scores = orc.index_topk(c, orc.REINDEX, inp["iq"][t][l], q_pos=self.q_pos[t],
+                                                     pool_in=pool, want_scores=want_scores)
+                out, _ = orc.attend(c, topk, self.swas[l], inp["q"][t][l], SM_SCALE, q_pos=self.q_pos[t])
+                res[t][l] = dict(topk=topk, pool=lpool, scores=scores, out=out)
+        return res
+
+
 def cpu_baseline(wl, steps=2):
     """The oracle, as it stands, on the first sequences of the same workload."""
     t0 = time.time()
-    ost = OracleStep(wl)
+    ost = OracleSchedule38(wl) if isinstance(wl, Schedule38) else OracleStep(wl)
     log(f"oracle sample set up in {time.time() - t0:.1f}s ({ost.hs} sequences)")
     times = []
     for s_i in range(steps):
@@ -352,6 +589,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload preset (synth.WORKLOADS)")
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--ctx", type=int, default=0, help="context tokens of the 38-layer schedule (0: the preset's)")
+    ap.add_argument("--batch", type=int, default=0, help="sequences of the 38-layer schedule (0: the preset's)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: all)")
@@ -378,8 +617,12 @@ def main():
     extra = args.warmup + args.steps + 4 * R + 8
     want_cpu = not args.no_cpu_baseline
     wl0 = synth.WORKLOADS[args.config]
-    hs = (args.cpu_seqs or wl0["B"]) if want_cpu else 0
-    wl = Workload(args.config, R, extra, keep_host_seqs=hs)
+    if wl0.get("schedule"):
+        hs = (args.cpu_seqs or 1) if want_cpu else 0
+        wl = Schedule38(args.config, args.batch or wl0["B"], args.ctx or wl0["ctx"], R, keep_host_seqs=hs)
+    else:
+        hs = (args.cpu_seqs or wl0["B"]) if want_cpu else 0
+        wl = Workload(args.config, R, extra, keep_host_seqs=hs)
 
     # ---- capture one graph per replica, and one graph that steps every replica
     # once (a cycle), so that a launch's fixed cost is paid once per R steps;
@@ -416,7 +659,7 @@ def main():
                 wl.step(i % R)
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
-    E_start = int(wl.caches[0].length.max().item())
+    E_start = int(wl.caches[0].length.max().item()) if wl.decode else 0
     log(f"warm-up done, timing {args.steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -427,7 +670,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    E_end = int(wl.caches[0].length.max().item())
+    E_end = int(wl.caches[0].length.max().item()) if wl.decode else 0
     ms_per_step = wall * 1e3 / args.steps
     value = wl.L * args.steps / wall
     E_mid = (E_start + E_end) // 2 if wl.decode else wl.ctx // wl.r
@@ -455,7 +698,10 @@ def main():
     # bytes: every indexer key of the batch once (the queries of a sequence share them);
     # FLOPs: 2 x 4 heads x 64 dims per (query, visible entry) pair
     idx_bytes = wl.B * E_idx * IDX_ROW
-    if wl.decode:
+    if isinstance(wl, Schedule38):
+        idx_bytes = wl.index_bytes()  # the decoder's Full call: one query per sequence
+        pairs = idx_bytes // IDX_ROW
+    elif wl.decode:
         pairs = wl.B * E_idx
     else:
         pos = wl.ctx - wl.Q + np.arange(wl.Q)
@@ -493,6 +739,8 @@ def main():
                    "queries_per_seq": wl.Q, "group": list(wl.group), "replicas": R,
                    "hipgraph": graphs is not None, "steps_per_graph_launch": R if graphs is not None else 0},
         "step_algorithmic_bytes": step_bytes, "step_GBps": round(step_gbps, 1),
+        **({"tokens_per_step": 2, "csa2_bytes_per_token_per_sequence": round(step_bytes / 2 / wl.B)}
+           if isinstance(wl, Schedule38) else {}),
         "step_frac_of_peak": round(step_gbps / PEAK_GBPS, 4),
         "roofline": roof, "cpu_baseline": cpu,
     }

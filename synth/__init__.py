@@ -32,6 +32,10 @@ WORKLOADS = {
     # query causal over the entries up to its own position
     5: dict(name="mtp_q6_f_ri_2ru_b16_ctx128k", B=16, ctx=131072, ratio=1, Q=6,
             group=("full_pool", "reindex", "reuse", "reuse")),
+    # the whole 38-layer schedule of a decode token: 3 x (Full + 5 Reuse) over
+    # ratio-2 encoder caches, then Full(+pool) + 3 Reuse and 4 x (Reindex + 3
+    # Reuse) over the ratio-1 decoder cache; two tokens per step
+    6: dict(name="sched38_b16_ctx128k", B=16, ctx=131072, ratio=1, Q=1, schedule=True, group=("schedule38",)),
 }
 
 
