@@ -50,8 +50,8 @@ class CacheStruct(ctypes.Structure):
                 ("capacity", ctypes.c_int32), ("ratio", ctypes.c_int32)]
 
 
-EXPORTS = ("csa2_quantize_append", "csa2_swa_append", "csa2_index_score_topk", "csa2_sparse_attend",
-           "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
+EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_swa_append", "csa2_index_score_topk",
+           "csa2_sparse_attend", "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
 
 
 def lib():
@@ -65,6 +65,8 @@ def lib():
         cp = ctypes.POINTER(CacheStruct)
         L.csa2_quantize_append.restype = ctypes.c_int
         L.csa2_quantize_append.argtypes = [cp, vp, vp, vp, i32, i32, vp]
+        L.csa2_quantize_append_proj.restype = ctypes.c_int
+        L.csa2_quantize_append_proj.argtypes = [cp, vp, vp, vp, i32, i32, vp]
         L.csa2_swa_append.restype = ctypes.c_int
         L.csa2_swa_append.argtypes = [vp, i32, vp, vp, i32, i32, vp]
         L.csa2_index_score_topk.restype = ctypes.c_int
@@ -153,6 +155,20 @@ def quantize_append(cache: Cache, kv, ik, logits=None, stream=None):
     rc = lib().csa2_quantize_append(ctypes.byref(st), _ptr(kv), _ptr(logits), _ptr(ik), T, cache.host_len_bound,
                                     _stream(stream))
     _check(rc, "csa2_quantize_append")
+    cache.host_len_bound += T // cache.ratio
+
+
+def quantize_append_proj(cache: Cache, kv, w_ik, logits=None, stream=None):
+    """csa2_quantize_append_proj: the new entries' indexer K is w_ik [512][64] applied to each entry."""
+    B, T = kv.shape[0], kv.shape[1]
+    _expect(kv, torch.float32, (cache.batch, T, D), "kv")
+    _expect(w_ik, torch.float32, (D, IDX_DIM), "w_ik")
+    if logits is not None:
+        _expect(logits, torch.float32, (cache.batch, T, D), "logits")
+    st = cache.struct()
+    rc = lib().csa2_quantize_append_proj(ctypes.byref(st), _ptr(kv), _ptr(logits), _ptr(w_ik), T,
+                                         cache.host_len_bound, _stream(stream))
+    _check(rc, "csa2_quantize_append_proj")
     cache.host_len_bound += T // cache.ratio
 
 

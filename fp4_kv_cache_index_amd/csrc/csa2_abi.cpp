@@ -46,8 +46,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
 
 extern "C" {
 
-int csa2_quantize_append(const csa2_cache* cache, const float* kv, const float* logits, const float* ik, int32_t T,
-                         int32_t host_len_bound, void* stream) {
+// the shared body of the two append calls: exactly one of ik and w_ik is given
+static int quantize_append_impl(const csa2_cache* cache, const float* kv, const float* logits, const float* ik,
+                                const float* w_ik, int32_t T, int32_t host_len_bound, void* stream) {
   int rc = check_cache(cache, true, true);
   if (rc != CSA2_OK) return rc;
   if (T < 0 || host_len_bound < 0) return CSA2_EINVAL;
@@ -56,9 +57,23 @@ int csa2_quantize_append(const csa2_cache* cache, const float* kv, const float* 
   const int64_t n_new = T / cache->ratio;
   if ((int64_t)host_len_bound + n_new > cache->capacity) return CSA2_ECAPACITY;
   if (cache->batch == 0 || T == 0) return CSA2_OK;
-  if (!kv || !ik || !aligned(kv, 16) || !aligned(ik, 4)) return CSA2_EINVAL;
+  if (!kv || !aligned(kv, 16)) return CSA2_EINVAL;
+  if ((ik == nullptr) == (w_ik == nullptr)) return CSA2_EINVAL;
+  if ((ik && !aligned(ik, 4)) || (w_ik && !aligned(w_ik, 4))) return CSA2_EINVAL;
   if (logits && !aligned(logits, 4)) return CSA2_EINVAL;
-  return from_hip(csa2::launch_quant_append(to_launch(cache), kv, logits, ik, T, (hipStream_t)stream));
+  return from_hip(csa2::launch_quant_append(to_launch(cache), kv, logits, ik, w_ik, T, (hipStream_t)stream));
+}
+
+int csa2_quantize_append(const csa2_cache* cache, const float* kv, const float* logits, const float* ik, int32_t T,
+                         int32_t host_len_bound, void* stream) {
+  if (!ik && cache && cache->batch > 0 && T > 0) return CSA2_EINVAL;
+  return quantize_append_impl(cache, kv, logits, ik, nullptr, T, host_len_bound, stream);
+}
+
+int csa2_quantize_append_proj(const csa2_cache* cache, const float* kv, const float* logits, const float* w_ik,
+                              int32_t T, int32_t host_len_bound, void* stream) {
+  if (!w_ik && cache && cache->batch > 0 && T > 0) return CSA2_EINVAL;
+  return quantize_append_impl(cache, kv, logits, nullptr, w_ik, T, host_len_bound, stream);
 }
 
 int csa2_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,

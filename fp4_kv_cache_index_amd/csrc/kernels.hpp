@@ -52,7 +52,7 @@ int attend_splits(int64_t bq);
 size_t attend_ws_bytes(int64_t bq);
 
 hipError_t launch_quant_append(const LaunchCache& c, const float* kv, const float* logits, const float* ik,
-                               int32_t T, hipStream_t stream);
+                               const float* w_ik, int32_t T, hipStream_t stream);
 hipError_t launch_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,
                              hipStream_t stream);
 hipError_t launch_index(const LaunchCache& c, int mode, const float* iq, const float* iw, const int32_t* q_pos,

@@ -193,6 +193,18 @@ def compress_pairs(x, z):
     return out
 
 
+def project_ik(entries, w_ik):
+    """Indexer K derived from main-KV entries (ai.info "Methodology in Plain
+    English": CSA2 takes indexer K from a projection of the main KV entries).
+    entries [..., 512] fp32, w_ik [512][64] fp32 channel-major:
+    k[d] = sum_c w_ik[c][d] * entry[c], each product exact in fp64, summed in
+    fp64 (a library matmul), rounded once to fp32."""
+    e = np.asarray(entries, np.float32).astype(np.float64)
+    w = np.asarray(w_ik, np.float32).astype(np.float64)
+    assert w.shape == (D, ID)
+    return (e @ w).astype(np.float32)
+
+
 def quantize_query(iq):
     iq = _c(iq, np.float32).reshape(IH, ID)
     q8 = np.empty((IH, ID), np.uint8)
@@ -233,6 +245,18 @@ def quantize_append(cache: Cache, kv, ik, logits=None):
                                    _p(cache.length, ctypes.c_int32), cache.B, cache.cap, cache.ratio,
                                    _p(kv, ctypes.c_float), _p(logits, ctypes.c_float), _p(ik, ctypes.c_float), T)
     _check(rc, "quantize_append")
+
+
+def quantize_append_proj(cache: Cache, kv, w_ik, logits=None):
+    """quantize_append with each new entry's indexer K = project_ik(entry), the
+    entry being the token row (ratio 1) or the compressed pair (ratio 2)."""
+    kv = _c(kv, np.float32)
+    if cache.ratio == 2:
+        logits = _c(logits, np.float32)
+        entries = np.stack([compress_pairs(kv[b], logits[b]) for b in range(kv.shape[0])])
+    else:
+        entries = kv
+    quantize_append(cache, kv, project_ik(entries, w_ik), logits=logits)
 
 
 def swa_append(swa, x, seq_len):

@@ -77,6 +77,23 @@ def test_append_rejections(csa):
     assert q(ctypes.byref(cache(csa)), p, None, p, 0, 0, None) == csa.OK  # nothing to do
 
 
+def test_append_proj_rejections(csa):
+    """The projected append validates like the plain one, and needs its w_ik."""
+    L = csa.lib()
+    p = ctypes.c_void_p(FAKE)
+    q = L.csa2_quantize_append_proj
+    assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=2)), p, p, p, 3, 0, None) == csa.EINVAL      # T % r
+    assert q(ctypes.byref(cache(csa, ratio=2)), p, None, p, 2, 0, None) == csa.EINVAL   # logits missing
+    assert q(ctypes.byref(cache(csa, cap=10)), p, None, p, 4, 7, None) == csa.ECAPACITY
+    assert q(ctypes.byref(cache(csa)), p, None, None, 1, 0, None) == csa.EINVAL          # no w_ik
+    assert q(ctypes.byref(cache(csa)), p, None, ctypes.c_void_p(FAKE + 2), 1, 0, None) == csa.EINVAL  # misaligned
+    assert q(ctypes.byref(cache(csa)), p, None, p, 0, 0, None) == csa.OK  # nothing to do
+    # and the plain append still needs its ik rows
+    assert L.csa2_quantize_append(ctypes.byref(cache(csa)), p, None, None, 1, 0, None) == csa.EINVAL
+
+
 def test_swa_rejections(csa):
     L = csa.lib()
     p = ctypes.c_void_p(FAKE)

@@ -85,6 +85,35 @@ def test_quantize_append_bitexact(csa, orc, B, T, ratio, pre):
     assert np.array_equal(host(gc.ik_scales).view(np.uint32), oc.ik_scales.view(np.uint32))
 
 
+@pytest.mark.parametrize("B,T,ratio", [
+    (3, 1, 1),       # decode: one entry per sequence
+    (2, 600, 1),     # several workgroups per sequence, second launch advances the lengths
+    (2, 2, 2),       # one compressed pair
+    (1, 1030, 2),    # 515 compressed entries
+])
+def test_quantize_append_proj_bitexact(csa, orc, B, T, ratio):
+    """Indexer K projected from each entry (w_ik [512][64]): every cache byte
+    equals the oracle's, over two calls in a row."""
+    n_new = T // ratio
+    cap = 2 * n_new + 5
+    w = (synth.normal(13, "w_ik", (512, 64)) / np.float32(math.sqrt(512.0))).astype(np.float32)
+    oc = orc.Cache(B, cap, ratio)
+    oc.length[:] = 2
+    gc = csa.Cache(B, cap, ratio)
+    gc.length.fill_(2)
+    gc.host_len_bound = 2
+    for call in range(2):
+        kv = special_rows(B * T).reshape(B, T, 512) if call == 0 else synth.normal(13, f"kv{T}", (B, T, 512))
+        logits = synth.normal(13, f"lg{T}_{call}", (B, T, 512)) * np.float32(2.0) if ratio == 2 else None
+        orc.quantize_append_proj(oc, kv, w, logits=logits)
+        csa.quantize_append_proj(gc, dev(kv), dev(w), logits=dev(logits) if logits is not None else None)
+        assert np.array_equal(host(gc.length), oc.length)
+        assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
+        assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
+        assert np.array_equal(host(gc.ik_codes), oc.ik_codes)
+        assert np.array_equal(host(gc.ik_scales).view(np.uint32), oc.ik_scales.view(np.uint32))
+
+
 def test_quantize_append_capacity(csa):
     gc = csa.Cache(2, 10, 1)
     kv = dev(synth.normal(13, "kv", (2, 4, 512)))
