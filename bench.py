@@ -266,8 +266,10 @@ class Schedule38:
     entry summarises two tokens, so the first token leaves it pending (the
     encoder layers see ctx / 2 entries) and the second completes it: each
     encoder Full layer appends the pair's entry before scoring.  The decoder
-    appends one entry per token.  Every step first resets the lengths, so each
-    step sees the same context.  76 layer-steps per step."""
+    appends one entry per token.  Every Full layer derives its indexer K by
+    projecting its main-KV entries (csa2_quantize_append_proj, seeded
+    N(0, 1/512) weights per cache).  Every step first resets the lengths, so
+    each step sees the same context.  76 layer-steps per step."""
 
     def __init__(self, cid, B, ctx, replicas, keep_host_seqs=0):
         import fp4_kv_cache_index_amd as csa
@@ -285,6 +287,9 @@ class Schedule38:
         self.ratio.update({n: 2 for n in ENC_CACHES})
         dev = "cuda"
         t0 = time.time()
+        self.w_ik_host = {n: (synth.normal(cid, f"w_ik_{n}", (512, 64)) / np.float32(math.sqrt(512.0)))
+                          .astype(np.float32) for n in self.E0}
+        self.w_ik = {n: torch.from_numpy(w).to(dev) for n, w in self.w_ik_host.items()}
         self.caches = [{n: csa.Cache(B, self.E0[n] + 8, self.ratio[n]) for n in self.E0} for _ in range(replicas)]
         hs = min(keep_host_seqs, B)
         self.host_rows = {} if hs else None
@@ -293,22 +298,18 @@ class Schedule38:
             r = self.ratio[n]
             if hs:
                 self.host_rows[n] = dict(kv=np.empty((hs, ctx, 512), np.float32),
-                                         ik=np.empty((hs, ctx // r, 64), np.float32),
                                          lg=np.empty((hs, ctx, 512), np.float32) if r == 2 else None)
             tok = 0
             while tok < ctx:
                 T = min(T_fill, ctx - tok)
                 kv = torch.stack([synth.torch_normal_rows(cid, f"kv_{n}", b * ROWS_PER_SEQ + tok, T, 512)
                                   for b in range(B)])
-                ik = torch.stack([synth.torch_normal_rows(cid, f"ik_{n}", b * ROWS_PER_SEQ + tok // r, T // r, 64)
-                                  for b in range(B)])
                 lg = (torch.stack([synth.torch_normal_rows(cid, f"lg_{n}", b * ROWS_PER_SEQ + tok, T, 512)
                                    for b in range(B)]) if r == 2 else None)
-                csa.quantize_append(c, kv, ik, logits=lg)
+                csa.quantize_append_proj(c, kv, self.w_ik[n], logits=lg)
                 if hs:
                     h = self.host_rows[n]
                     h["kv"][:, tok:tok + T] = kv[:hs].cpu().numpy()
-                    h["ik"][:, tok // r:(tok + T) // r] = ik[:hs].cpu().numpy()
                     if r == 2:
                         h["lg"][:, tok:tok + T] = lg[:hs].cpu().numpy()
                 tok += T
@@ -345,9 +346,8 @@ class Schedule38:
             g = f"s38step{i}"
             inp = dict(
                 # encoder pair (2 tokens -> 1 entry) appended at the second token
-                enc={n: dict(kv=rows(g + "kv" + n, 2, 512), lg=rows(g + "lg" + n, 2, 512), ik=rows(g + "ik" + n, 1, 64))
-                     for n in ENC_CACHES},
-                dec=[dict(kv=rows(g + f"kvdec{t}", 1, 512), ik=rows(g + f"ikdec{t}", 1, 64)) for t in range(2)],
+                enc={n: dict(kv=rows(g + "kv" + n, 2, 512), lg=rows(g + "lg" + n, 2, 512)) for n in ENC_CACHES},
+                dec=[dict(kv=rows(g + f"kvdec{t}", 1, 512)) for t in range(2)],
                 x=[[rows(g + f"x{t}_{l}", 1, 512) for l in range(nL)] for t in range(2)],
                 iq=[[(rows(g + f"iq{t}_{l}", 4, 64).reshape(B, 1, 4, 64).contiguous()
                       if SCHEDULE38[l][0] != "reuse" else None) for l in range(nL)] for t in range(2)],
@@ -381,8 +381,8 @@ class Schedule38:
             if t == 1:
                 for n in ENC_CACHES:
                     e = inp["enc"][n]
-                    csa.quantize_append(cs[n], e["kv"], e["ik"], logits=e["lg"])
-            csa.quantize_append(cs["dec"], inp["dec"][t]["kv"], inp["dec"][t]["ik"])
+                    csa.quantize_append_proj(cs[n], e["kv"], self.w_ik[n], logits=e["lg"])
+            csa.quantize_append_proj(cs["dec"], inp["dec"][t]["kv"], self.w_ik["dec"])
             topk = None
             for l, (mode, cn) in enumerate(SCHEDULE38):
                 c = cs[cn]
@@ -439,7 +439,7 @@ class OracleSchedule38:
         self.oc = {}
         for n, h in wl.host_rows.items():
             c = orc.Cache(hs, wl.caches[0][n].capacity, wl.ratio[n])
-            orc.quantize_append(c, h["kv"], h["ik"], logits=h["lg"])
+            orc.quantize_append_proj(c, h["kv"], wl.w_ik_host[n], logits=h["lg"])
             self.oc[n] = c
         self.swas = []
         for l in range(len(SCHEDULE38)):
@@ -465,8 +465,8 @@ class OracleSchedule38:
             if t == 1:
                 for n in ENC_CACHES:
                     e = inp["enc"][n]
-                    orc.quantize_append(oc[n], e["kv"], e["ik"], logits=e["lg"])
-            orc.quantize_append(oc["dec"], inp["dec"][t]["kv"], inp["dec"][t]["ik"])
+                    orc.quantize_append_proj(oc[n], e["kv"], wl.w_ik_host[n], logits=e["lg"])
+            orc.quantize_append_proj(oc["dec"], inp["dec"][t]["kv"], wl.w_ik_host["dec"])
             seq = np.full(self.hs, wl.ctx + t + 1, np.int32)
             topk, pool = None, None
             for l, (mode, cn) in enumerate(SCHEDULE38):
