@@ -25,10 +25,12 @@ def gpu():
     return csa
 
 
-@pytest.mark.parametrize("B,ctx", [(2, 4096), (1, 40000)])
-def test_schedule38_step(gpu, B, ctx):
+# (sequences, context, sequences the oracle replays): two small cases compared
+# whole, and the benchmark's 16 x 128K workload sampled on its first sequence
+@pytest.mark.parametrize("B,ctx,hs", [(2, 4096, 2), (1, 40000, 1), (16, 131072, 1)])
+def test_schedule38_step(gpu, B, ctx, hs):
     print(f"schedule38 B={B} ctx={ctx}: building", flush=True)
-    wl = bench.Schedule38(6, B, ctx, replicas=1, keep_host_seqs=B)
+    wl = bench.Schedule38(6, B, ctx, replicas=1, keep_host_seqs=hs)
     wl.step(0, record=True)
     torch.cuda.synchronize()
     print("GPU step done, running the oracle", flush=True)
@@ -36,34 +38,35 @@ def test_schedule38_step(gpu, B, ctx):
     res = ost.step(want_scores=True)
     for n, c in wl.caches[0].items():
         oc = ost.oc[n]
-        assert np.array_equal(c.length.cpu().numpy(), oc.length), n
+        assert np.array_equal(c.length[:hs].cpu().numpy(), oc.length), n
         m = int(oc.length.max())
         for f in ("kv_codes", "kv_scales", "ik_codes"):
-            assert np.array_equal(getattr(c, f)[:, :m].cpu().numpy(), getattr(oc, f)[:, :m]), (n, f)
+            assert np.array_equal(getattr(c, f)[:hs, :m].cpu().numpy(), getattr(oc, f)[:, :m]), (n, f)
+        assert np.array_equal(c.ik_scales[:hs, :m].cpu().numpy().view(np.uint32), oc.ik_scales[:, :m].view(np.uint32))
     swaps, compared = 0, 0
     for t in range(2):
         for l, (mode, cn) in enumerate(bench.SCHEDULE38):
             r = res[t][l]
             used = wl.used[t][l].cpu().numpy()
             if mode != "reuse":
-                for b in range(B):
+                for b in range(hs):
                     swaps += topk_swaps(used[b, 0], r["topk"][b, 0], r["scores"][b, 0], name=f"t{t} L{l} b{b}")
             if mode == "full_pool":
                 pool = wl.used_pool[t].cpu().numpy()
-                for b in range(B):
+                for b in range(hs):
                     n_vis = wl.ctx + t + 1  # decoder entries visible to token t
                     swaps += pool_block_swaps(pool[b, 0], r["pool"][b, 0], r["scores"][b, 0], n_vis,
                                               name=f"t{t} pool b{b}")
             got = wl.out[t][l].float().cpu().numpy()
-            for b in range(B):
+            for b in range(hs):
                 # the oracle attends with its own Top-K; compare where the sets agree
                 if set(used[b, 0].tolist()) != set(r_topk(res[t], l)[b, 0].tolist()):
                     continue
                 attn_close(got[b, 0], r["out"][b, 0], name=f"t{t} L{l} b{b}")
                 compared += 1
-    print(f"schedule38 B={B} ctx={ctx}: {compared} of {2 * 38 * B} attention outputs compared, "
+    print(f"schedule38 B={B} ctx={ctx}: {compared} of {2 * 38 * hs} attention outputs compared, "
           f"{swaps} boundary swaps", flush=True)
-    assert compared >= 2 * 38 * B - 4 * B * 10  # nearly all: a swap changes one layer group at most
+    assert compared >= 2 * 38 * hs - 4 * hs * 10  # nearly all: a swap changes one layer group at most
 
 
 def r_topk(res_t, l):
