@@ -191,7 +191,7 @@ def test_index_full_topk_and_pool(csa, orc, E):
     print(f"E={E}: boundary swaps {swaps}")
 
 
-@pytest.mark.parametrize("nq", [4, 9])  # one group of four queries per workgroup / groups of eight, ragged
+@pytest.mark.parametrize("nq", [4, 6, 9])  # one group of four queries per workgroup / eight (6 used) / 8 + 1
 def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
     B, E, ratio = 2, 5000, 2
     cap = 5003
@@ -209,6 +209,22 @@ def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
             n_vis = min(int(oc.length[b]), (int(q_pos[b, q]) + 1) // ratio)
             topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"topk b{b} q{q}")
             pool_block_swaps(pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
+
+
+def test_index_full_prefill_chunk_no_pool(csa, orc):
+    """A 70-query chunk without a pool: eight workgroups of 8 queries and a
+    ragged ninth share each chunk's key loads; every query is causal."""
+    B, E = 2, 6000
+    oc = oracle_cache_ik(orc, B, E + 3, [E, 5100], 23)
+    Q = 70
+    q_pos = np.array([[E - Q + q for q in range(Q)], [5100 - 2 * Q + 2 * q for q in range(Q)]], np.int32)
+    iq = synth.normal(23, "iq", (B, Q, 4, 64))
+    ref_topk, _, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_scores=True)
+    gc = upload(csa, oc)
+    topk, _ = run_full(csa, gc, iq, q_pos=q_pos, want_pool=False)
+    for b in range(B):
+        for q in range(Q):
+            topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"topk b{b} q{q}")
 
 
 # selection inside the final kernel / entries through the filter kernel / 8,750 tied pool blocks, more
