@@ -165,12 +165,12 @@ def upload(csa, oc, with_main=False):
     return gc
 
 
-def run_full(csa, gc, iq, q_pos=None, want_pool=True):
+def run_full(csa, gc, iq, q_pos=None, want_pool=True, iw=None):
     B, Q = iq.shape[0], iq.shape[1]
     topk = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
     pool = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device="cuda") if want_pool else None
     csa.index_score_topk(gc, csa.FULL, dev(iq), topk, q_pos=dev(q_pos) if q_pos is not None else None,
-                         pool_out=pool)
+                         pool_out=pool, iw=dev(iw) if iw is not None else None)
     return host(topk), host(pool) if want_pool else None
 
 
@@ -201,9 +201,11 @@ def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
     q_pos = np.ascontiguousarray(q_pos[:, -nq:])
     Q = q_pos.shape[1]
     iq = synth.normal(21, "iq", (B, Q, 4, 64))
-    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_pool=True, want_scores=True)
+    iw = synth.uniform(21, "iw", (B, Q, 4), 0.25, 2.0)  # head weights, per query
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, iw=iw, q_pos=q_pos, want_pool=True,
+                                                want_scores=True)
     gc = upload(csa, oc)
-    topk, pool = run_full(csa, gc, iq, q_pos=q_pos)
+    topk, pool = run_full(csa, gc, iq, q_pos=q_pos, iw=iw)
     for b in range(B):
         for q in range(Q):
             n_vis = min(int(oc.length[b]), (int(q_pos[b, q]) + 1) // ratio)
