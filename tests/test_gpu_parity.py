@@ -296,13 +296,17 @@ def test_index_reindex(csa, orc, E):
         assert set(got[b, 0].tolist()) == set(ref_full[b, 0].tolist())
 
 
-def test_index_deterministic(csa, orc):
+@pytest.mark.parametrize("Q", [1, 6])  # one-query scorer / eight-query scorer; both through the filter
+def test_index_deterministic(csa, orc, Q):
+    """Repeated calls give identical Top-K lists and pools, although the filter
+    writes its candidates in an order set by atomics."""
     B, E = 2, 30000
     oc = oracle_cache_ik(orc, B, E, [E, E], 25)
     gc = upload(csa, oc)
-    iq = synth.normal(25, "iq", (B, 1, 4, 64))
-    a = run_full(csa, gc, iq)
-    b = run_full(csa, gc, iq)
+    iq = synth.normal(25, "iq", (B, Q, 4, 64))
+    q_pos = np.array([[E - Q + q for q in range(Q)]] * B, np.int32)
+    a = run_full(csa, gc, iq, q_pos=q_pos)
+    b = run_full(csa, gc, iq, q_pos=q_pos)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
