@@ -6,6 +6,7 @@ meaning, layout and ownership of every argument, is include/csa2.h; the
 function names here are the same.  If the library is not built this module
 raises on first use: there is no fallback path.
 """
+import contextlib
 import ctypes
 import os
 
@@ -33,9 +34,13 @@ ECAPACITY = -2
 EWORKSPACE = -3
 EUNSUPPORTED = -4
 EHIP = -5
+EDEVICE = -6  # debug library: an earlier call found a device precondition violated
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+# the same library with the kernels' device-side precondition checks on
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2_debug.so")
 _lib = None
+_debug_lib = None
 
 
 class CSA2Error(RuntimeError):
@@ -54,33 +59,59 @@ EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_swa_append
            "csa2_sparse_attend", "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
 
 
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cp = ctypes.POINTER(CacheStruct)
+    L.csa2_quantize_append.restype = ctypes.c_int
+    L.csa2_quantize_append.argtypes = [cp, vp, vp, vp, i32, i32, vp]
+    L.csa2_quantize_append_proj.restype = ctypes.c_int
+    L.csa2_quantize_append_proj.argtypes = [cp, vp, vp, vp, i32, i32, vp]
+    L.csa2_swa_append.restype = ctypes.c_int
+    L.csa2_swa_append.argtypes = [vp, i32, vp, vp, i32, i32, vp]
+    L.csa2_index_score_topk.restype = ctypes.c_int
+    L.csa2_index_score_topk.argtypes = [cp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.csa2_sparse_attend.restype = ctypes.c_int
+    L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz, vp]
+    L.csa2_workspace_bytes.restype = sz
+    L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32]
+    L.csa2_status_string.restype = ctypes.c_char_p
+    L.csa2_status_string.argtypes = [ctypes.c_int]
+    L.csa2_version.restype = ctypes.c_char_p
+    return L
+
+
 def lib():
-    """Load libcsa2.so (built in-tree by __graft_entry__.build())."""
+    """Load libcsa2.so (built in-tree by __graft_entry__.build()), or the debug
+    library when the environment sets CSA2_DEBUG=1."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        cp = ctypes.POINTER(CacheStruct)
-        L.csa2_quantize_append.restype = ctypes.c_int
-        L.csa2_quantize_append.argtypes = [cp, vp, vp, vp, i32, i32, vp]
-        L.csa2_quantize_append_proj.restype = ctypes.c_int
-        L.csa2_quantize_append_proj.argtypes = [cp, vp, vp, vp, i32, i32, vp]
-        L.csa2_swa_append.restype = ctypes.c_int
-        L.csa2_swa_append.argtypes = [vp, i32, vp, vp, i32, i32, vp]
-        L.csa2_index_score_topk.restype = ctypes.c_int
-        L.csa2_index_score_topk.argtypes = [cp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
-        L.csa2_sparse_attend.restype = ctypes.c_int
-        L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz,
-                                            vp]
-        L.csa2_workspace_bytes.restype = sz
-        L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32]
-        L.csa2_status_string.restype = ctypes.c_char_p
-        L.csa2_status_string.argtypes = [ctypes.c_int]
-        L.csa2_version.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(DEBUG_LIB_PATH if os.environ.get("CSA2_DEBUG") == "1" else LIB_PATH)
     return _lib
+
+
+def debug_lib():
+    """The debug library (device-side precondition checks, CSA2_EDEVICE on the
+    next call after a violation), loaded beside the release one."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+@contextlib.contextmanager
+def using(L):
+    """Route this module's calls through the library handle L (say debug_lib())
+    inside the block."""
+    global _lib
+    prev = lib()
+    _lib = L
+    try:
+        yield L
+    finally:
+        _lib = prev
 
 
 def status_string(status: int) -> str:

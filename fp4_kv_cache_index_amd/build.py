@@ -1,4 +1,5 @@
-"""Build libcsa2.so (the gfx950 HIP kernels plus the C-ABI) in-tree with hipcc."""
+"""Build libcsa2.so (the gfx950 HIP kernels plus the C-ABI) in-tree with hipcc, and
+libcsa2_debug.so, the same library with the device-side precondition checks on."""
 import os
 import subprocess
 import sys
@@ -7,8 +8,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa2.so")
+DEBUG_LIB = os.path.join(HERE, "libcsa2_debug.so")
 SOURCES = ["quant_append.hip", "index.hip", "attend.hip", "csa2_abi.cpp"]
-HEADERS = ["codec.hpp", "kernels.hpp", "block_ops.hpp"]
+HEADERS = ["codec.hpp", "kernels.hpp", "block_ops.hpp", "dev_check.hpp"]
 ARCH = "gfx950"
 
 
@@ -17,15 +19,20 @@ def sources():
         os.path.join(INCLUDE, "csa2.h")]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    build_dir = os.path.join(HERE, "_build")
+    build_dir = os.path.join(HERE, "_build", "debug" if debug else "release")
+    lib = DEBUG_LIB if debug else LIB
     os.makedirs(build_dir, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-Wall",
               # keep the compiler from forming packed fp32 instructions
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               # IEEE fp32 division and sqrt (the quantisers divide by the scale)
               "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=fast"]
+    if debug:
+        # the checks on, and the internal namespace renamed, so that the two
+        # libraries can be loaded into one process side by side
+        common += ["-DCSA2_DEBUG", "-Dcsa2=csa2_debug"]
     objs = []
     procs = []
     for s in SOURCES:
@@ -44,14 +51,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for p, name in procs:
         if p.wait() != 0:
             raise RuntimeError(f"hipcc failed on {name}")
-    link = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", LIB + ".tmp"] + objs
+    link = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", lib + ".tmp"] + objs
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, debug=True)
     sys.exit(0)

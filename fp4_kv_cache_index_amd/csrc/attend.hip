@@ -33,6 +33,7 @@
 
 #include "block_ops.hpp"
 #include "codec.hpp"
+#include "dev_check.hpp"
 #include "kernels.hpp"
 
 namespace csa2 {
@@ -151,6 +152,16 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
   // new window tokens are positions new_lo .. new_hi-1
   const int32_t new_hi = a.swa_x ? a.swa_len[b] : 0;
   const int32_t new_lo = a.swa_x ? new_hi - a.swa_T : 0;
+  // debug builds: the entries this query may list; a listed id at or past them
+  // is flagged and skipped
+  int32_t n_vis_dbg = 0;
+  if (kDebug) {
+    const int32_t len = a.length[b];
+    if (tid == 0 && split == 0 && (len < 0 || len > a.cap)) dev_flag(kErrLength);
+    if (tid == 0 && split == 0 && new_lo < 0) dev_flag(kErrSeqLen);
+    const int64_t by_pos = p < 0 ? 0 : ((int64_t)p + 1) / a.ratio;
+    n_vis_dbg = (int32_t)min((int64_t)min(len, a.cap), by_pos);
+  }
 
   const int t_begin = split * a.tps;
   const int t_end = min(kTilesPerQuery, t_begin + a.tps);
@@ -177,7 +188,14 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
     const bool mine = tile < t_end;                 // uniform: tiles past the split hold nothing
     const bool main_tile = tile * kAttnTile < 512;  // uniform: 512 is a multiple of the tile
     const bool rows = main_tile && a.cap > 0 && mine;  // uniform
-    const int32_t es[4] = {mine ? e4.x : -1, mine ? e4.y : -1, mine ? e4.z : -1, mine ? e4.w : -1};
+    int32_t es[4] = {mine ? e4.x : -1, mine ? e4.y : -1, mine ? e4.z : -1, mine ? e4.w : -1};
+    if (kDebug && main_tile && mine)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (es[i] < -1 || es[i] >= n_vis_dbg) {
+          dev_flag(kErrEntryId);
+          es[i] = -1;
+        }
     vmask = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -253,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
         if (j < a.swa_T) {
           const uint16_t c = (uint16_t)(e4m3_encode(xv[j].x) | (e4m3_encode(xv[j].y) << 8));
           reinterpret_cast<uint16_t*>(s_new + j * 512)[tid] = c;
-          if (j % n_w == rank)
+          if (j % n_w == rank && new_lo + j >= 0)  // a window shorter than the append has no slot for it
             reinterpret_cast<uint16_t*>(a.swa + ((int64_t)b * a.S + (new_lo + j) % a.S) * 512)[tid] = c;
         }
       }
@@ -484,6 +502,8 @@ __global__ void __launch_bounds__(kThreads)
   reinterpret_cast<uint32_t*>(out + (bq * 16 + h) * 512)[tid] = packed;
   if (lse && tid == 0) lse[bq * 16 + h] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
+
+CSA2_DEV_ERROR_TAKER(take_attend_dev_error)
 
 hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
                          const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos,

@@ -42,6 +42,17 @@ csa2::LaunchCache to_launch(const csa2_cache* c) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
 
+// Debug library: a precondition violation that an earlier call's kernels
+// recorded on this device (read once the stream's earlier work is done) is
+// reported as CSA2_EDEVICE, and the record cleared, by the next call that has
+// work to enqueue.  The release library returns CSA2_OK without touching the
+// GPU.
+int device_status(void* stream) {
+  const hipStream_t s = (hipStream_t)stream;
+  const uint32_t e = csa2::take_append_dev_error(s) | csa2::take_index_dev_error(s) | csa2::take_attend_dev_error(s);
+  return e ? CSA2_EDEVICE : CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,6 +72,7 @@ static int quantize_append_impl(const csa2_cache* cache, const float* kv, const 
   if ((ik == nullptr) == (w_ik == nullptr)) return CSA2_EINVAL;
   if ((ik && !aligned(ik, 4)) || (w_ik && !aligned(w_ik, 4))) return CSA2_EINVAL;
   if (logits && !aligned(logits, 4)) return CSA2_EINVAL;
+  if ((rc = device_status(stream)) != CSA2_OK) return rc;
   return from_hip(csa2::launch_quant_append(to_launch(cache), kv, logits, ik, w_ik, T, (hipStream_t)stream));
 }
 
@@ -81,6 +93,8 @@ int csa2_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_
   if (S < 1 || B < 0 || T < 0 || T > S) return CSA2_EINVAL;
   if (B == 0 || T == 0) return CSA2_OK;
   if (!swa || !x || !seq_len || !aligned(swa, 4) || !aligned(x, 16) || !aligned(seq_len, 4)) return CSA2_EINVAL;
+  const int rc = device_status(stream);
+  if (rc != CSA2_OK) return rc;
   return from_hip(csa2::launch_swa_append(swa, S, x, seq_len, B, T, (hipStream_t)stream));
 }
 
@@ -104,6 +118,7 @@ int csa2_index_score_topk(const csa2_cache* cache, int mode, const float* iq, co
     return CSA2_EINVAL;
   const size_t need = csa2_workspace_bytes(CSA2_OP_INDEX, cache->batch, Q, cache->capacity);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  if ((rc = device_status(stream)) != CSA2_OK) return rc;
   return from_hip(csa2::launch_index(to_launch(cache), mode, iq, iw, q_pos, pool_in, topk_out, pool_out, Q, ws,
                                      (hipStream_t)stream));
 }
@@ -119,6 +134,7 @@ int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, uint8_t* sw
   if (swa_x && (!swa || !aligned(swa, 16) || !aligned(swa_x, 16) || !aligned(swa_len, 4))) return CSA2_EINVAL;
   if (Q == 0) {  // no query: only the window append, if any
     if (!swa_x) return CSA2_OK;
+    if ((rc = device_status(stream)) != CSA2_OK) return rc;
     return from_hip(csa2::launch_swa_append(swa, S, swa_x, swa_len, cache->batch, swa_T, (hipStream_t)stream));
   }
   if (!topk || !swa || !q || !out) return CSA2_EINVAL;
@@ -126,6 +142,7 @@ int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, uint8_t* sw
   if ((lse && !aligned(lse, 4)) || (q_pos && !aligned(q_pos, 4))) return CSA2_EINVAL;
   const size_t need = csa2_workspace_bytes(CSA2_OP_ATTEND, cache->batch, Q, cache->capacity);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  if ((rc = device_status(stream)) != CSA2_OK) return rc;
   return from_hip(csa2::launch_attend(to_launch(cache), topk, swa, S, swa_x, swa_len, swa_T, q, q_pos, sm_scale, out,
                                       lse, Q, ws, (hipStream_t)stream));
 }
@@ -146,10 +163,15 @@ const char* csa2_status_string(int status) {
     case CSA2_EWORKSPACE: return "workspace missing or too small";
     case CSA2_EUNSUPPORTED: return "unsupported request";
     case CSA2_EHIP: return "HIP launch failed";
+    case CSA2_EDEVICE: return "an earlier call found a device precondition violated (debug library)";
     default: return "unknown status";
   }
 }
 
+#ifdef CSA2_DEBUG
+const char* csa2_version(void) { return "csa2-gfx950 0.1 debug"; }
+#else
 const char* csa2_version(void) { return "csa2-gfx950 0.1"; }
+#endif
 
 }  // extern "C"

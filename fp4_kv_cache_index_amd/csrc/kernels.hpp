@@ -51,6 +51,19 @@ constexpr int kAttnTile = 32;
 int attend_splits(int64_t bq);
 size_t attend_ws_bytes(int64_t bq);
 
+// ---- device precondition violations a debug build records (dev_check.hpp)
+enum : uint32_t {
+  kErrLength = 1u,       // length[b] above the capacity, or negative
+  kErrEntryId = 2u,      // a Top-K id at or past the entries visible to its query
+  kErrPoolId = 4u,       // a Reindex pool entry at or past the entries visible to its query
+  kErrSeqLen = 8u,       // a window length smaller than the tokens appended
+  kErrCapacity = 16u,    // an append that would pass the capacity (not made)
+  kErrUnreadable = 1u << 31,  // the word itself could not be read or cleared
+};
+uint32_t take_append_dev_error(hipStream_t stream);
+uint32_t take_index_dev_error(hipStream_t stream);
+uint32_t take_attend_dev_error(hipStream_t stream);
+
 hipError_t launch_quant_append(const LaunchCache& c, const float* kv, const float* logits, const float* ik,
                                const float* w_ik, int32_t T, hipStream_t stream);
 hipError_t launch_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,

@@ -34,10 +34,31 @@ def test_exports_every_declared_symbol(csa):
 
 
 def test_status_strings_and_version(csa):
-    for code in (csa.OK, csa.EINVAL, csa.ECAPACITY, csa.EWORKSPACE, csa.EUNSUPPORTED, csa.EHIP):
+    for code in (csa.OK, csa.EINVAL, csa.ECAPACITY, csa.EWORKSPACE, csa.EUNSUPPORTED, csa.EHIP, csa.EDEVICE):
         assert csa.status_string(code) and csa.status_string(code) != "unknown status"
     assert csa.status_string(12345) == "unknown status"
-    assert "gfx950" in csa.version()
+    assert "gfx950" in csa.version() and not csa.version().endswith("debug")
+
+
+def test_debug_library_exports_and_version(csa):
+    """The debug library exports the same symbols, says it is the debug build,
+    and keeps its internals in a namespace of its own (both load side by side)."""
+    D = csa.debug_lib()
+    for s in declared_symbols():
+        assert hasattr(D, s), s
+    assert D.csa2_version().decode().endswith("debug")
+    assert D.csa2_workspace_bytes(csa.OP_INDEX, 16, 1, 131072) == csa.workspace_bytes(csa.OP_INDEX, 16, 1, 131072)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.DEBUG_LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        assert "10csa2_debug" in out.stdout and "4csa2" not in out.stdout  # mangled namespace names
+
+
+@pytest.fixture(params=["release", "debug"])
+def L(request, csa):
+    """Each host-validation test runs against both libraries: the debug one
+    validates exactly as the release one does."""
+    return csa.lib() if request.param == "release" else csa.debug_lib()
 
 
 def test_workspace_sizes(csa):
@@ -60,8 +81,7 @@ def cache(csa, B=2, cap=100, ratio=1, **over):
     return c
 
 
-def test_append_rejections(csa):
-    L = csa.lib()
+def test_append_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     q = L.csa2_quantize_append
     assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
@@ -77,9 +97,8 @@ def test_append_rejections(csa):
     assert q(ctypes.byref(cache(csa)), p, None, p, 0, 0, None) == csa.OK  # nothing to do
 
 
-def test_append_proj_rejections(csa):
+def test_append_proj_rejections(csa, L):
     """The projected append validates like the plain one, and needs its w_ik."""
-    L = csa.lib()
     p = ctypes.c_void_p(FAKE)
     q = L.csa2_quantize_append_proj
     assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
@@ -94,8 +113,7 @@ def test_append_proj_rejections(csa):
     assert L.csa2_quantize_append(ctypes.byref(cache(csa)), p, None, None, 1, 0, None) == csa.EINVAL
 
 
-def test_swa_rejections(csa):
-    L = csa.lib()
+def test_swa_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     s = L.csa2_swa_append
     assert s(p, 0, p, p, 1, 1, None) == csa.EINVAL
@@ -105,8 +123,7 @@ def test_swa_rejections(csa):
     assert s(p, 128, p, p, 0, 1, None) == csa.OK
 
 
-def test_index_rejections(csa):
-    L = csa.lib()
+def test_index_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     f = L.csa2_index_score_topk
     c = ctypes.byref(cache(csa, cap=131072))
@@ -123,8 +140,7 @@ def test_index_rejections(csa):
     assert f(c, csa.FULL, p, None, None, None, p, None, 0, None, 0, None) == csa.OK
 
 
-def test_attend_rejections(csa):
-    L = csa.lib()
+def test_attend_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     a = L.csa2_sparse_attend
     c = ctypes.byref(cache(csa, B=16))
