@@ -500,8 +500,25 @@ def cpu_baseline(wl, steps=2):
     t_step = float(np.median(times))
     value = wl.L / t_step * ost.hs / wl.B
     return dict(value=value, unit=UNIT, cores=int(min(ost.orc.num_threads(), ost.hs * wl.Q)), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"{steps} group steps of the first {ost.hs} of {wl.B} sequences (full context, all {wl.L} "
                        f"layers), median {t_step:.2f}s per step, scaled by {wl.B}/{ost.hs} to the whole batch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def pct(xs):
+    """p10, median and p90 of a list of µs figures."""
+    return [round(float(np.percentile(xs, q)), 2) for q in (10, 50, 90)]
 
 
 COPY_BYTES = 256 << 20
@@ -614,7 +631,9 @@ def main():
     import fp4_kv_cache_index_amd as csa
     csa.lib()
     R = max(1, args.replicas)
-    extra = args.warmup + args.steps + 4 * R + 8
+    # appends per replica: warm-up, timed steps and the spread pass (R >= 2 replicas
+    # share them, so warm-up + steps covers all three)
+    extra = args.warmup + args.steps * (2 if R == 1 else 1) + 4 * R + 8
     want_cpu = not args.no_cpu_baseline
     wl0 = synth.WORKLOADS[args.config]
     if wl0.get("schedule"):
@@ -644,9 +663,12 @@ def main():
                 wl.step(i)
         torch.cuda.synchronize()
 
-        def run_steps(i0, n):  # steps i0 .. i0 + n - 1, replica i % R each
+        def run_steps(i0, n, marks=None):  # steps i0 .. i0 + n - 1, replica i % R each
             i = i0
             while i < i0 + n:
+                if marks is not None:
+                    marks.append((i, torch.cuda.Event(enable_timing=True)))
+                    marks[-1][1].record()
                 if i % R == 0 and i + R <= i0 + n:
                     cycle.replay()
                     i += R
@@ -654,8 +676,11 @@ def main():
                     graphs[i % R].replay()
                     i += 1
     else:
-        def run_steps(i0, n):
+        def run_steps(i0, n, marks=None):
             for i in range(i0, i0 + n):
+                if marks is not None:
+                    marks.append((i, torch.cuda.Event(enable_timing=True)))
+                    marks[-1][1].record()
                 wl.step(i % R)
     run_steps(0, args.warmup)
     torch.cuda.synchronize()
@@ -671,6 +696,16 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     E_end = int(wl.caches[0].length.max().item()) if wl.decode else 0
+    # the spread: the same steps again, untimed above, with an event before each
+    # graph launch (the events stay out of the timed region)
+    marks = []
+    i_sp = args.warmup + args.steps
+    run_steps(i_sp, args.steps, marks)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    ev_end.record()
+    torch.cuda.synchronize()
+    bounds = marks + [(i_sp + args.steps, ev_end)]
+    step_us = [a[1].elapsed_time(b[1]) * 1e3 / (b[0] - a[0]) for a, b in zip(bounds, bounds[1:])]
     ms_per_step = wall * 1e3 / args.steps
     value = wl.L * args.steps / wall
     E_mid = (E_start + E_end) // 2 if wl.decode else wl.ctx // wl.r
@@ -715,7 +750,8 @@ def main():
         achieved = idx_bytes / t_idx / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_GBPS, 4), traffic=traffic, kernel=kernel_name,
-                    bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2))
+                    bytes_per_launch=idx_bytes, avg_launch_us=round(t_idx * 1e6, 2),
+                    launch_us_p10_p50_p90=pct([d * 1e6 for d in durs]))
         log(f"Full indexer call: {t_idx * 1e6:.1f} us, {achieved:.0f} GB/s on {idx_bytes / 1e6:.1f} MB")
     else:
         # a prefill chunk scores every query against every entry it sees: a dense
@@ -723,7 +759,8 @@ def main():
         tflops = flops / t_idx / 1e12
         roof = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=kernel_name,
-                    flops_per_launch=flops, avg_launch_us=round(t_idx * 1e6, 2))
+                    flops_per_launch=flops, avg_launch_us=round(t_idx * 1e6, 2),
+                    launch_us_p10_p50_p90=pct([d * 1e6 for d in durs]))
         log(f"Full indexer call: {t_idx * 1e6:.1f} us, {tflops:.1f} TFLOP/s on {flops / 1e9:.2f} GFLOP")
 
     if args.copy_calibration:
@@ -734,6 +771,7 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "step_us_p10_p50_p90": pct(step_us),
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context_tokens": wl.ctx, "ratio": wl.r,
                    "queries_per_seq": wl.Q, "group": list(wl.group), "replicas": R,
