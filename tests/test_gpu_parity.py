@@ -191,6 +191,35 @@ def test_index_full_topk_and_pool(csa, orc, E):
     print(f"E={E}: boundary swaps {swaps}")
 
 
+@pytest.mark.parametrize("Q", [1, 6])  # the one-query scorer / the eight-query scorer
+def test_index_empty_sequences(csa, orc, Q):
+    """Sequences with no entry, and queries placed before the first entry, get
+    an all -1 Top-K and pool; their neighbour with entries is unaffected; and
+    Reindex over an empty pool gives all -1."""
+    B, cap = 3, 40
+    lengths = [0, 30, 0]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 26)
+    iq = synth.normal(26, f"iq{Q}", (B, Q, 4, 64))
+    mid = [29] if Q == 1 else [-1, 0, 5, 10, 20, 29]
+    q_pos = np.array([[q - 1 for q in range(Q)], mid, [q - 1 for q in range(Q)]], np.int32)
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq, q_pos=q_pos)
+    for b in (0, 2):
+        assert (topk[b] == -1).all() and (pool[b] == -1).all()
+    for q in range(Q):
+        if q_pos[1, q] < 0:
+            assert (topk[1, q] == -1).all() and (pool[1, q] == -1).all()
+        else:
+            topk_swaps(topk[1, q], ref_topk[1, q], scores[1, q], name=f"q{q}")
+            n_vis = min(30, int(q_pos[1, q]) + 1)
+            pool_block_swaps(pool[1, q], ref_pool[1, q], scores[1, q], n_vis, name=f"pool q{q}")
+    empty = np.full((B, Q, csa.POOL), -1, np.int32)
+    rt = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.REINDEX, dev(iq), rt, q_pos=dev(q_pos), pool_in=dev(empty))
+    assert (host(rt) == -1).all()
+
+
 @pytest.mark.parametrize("nq", [4, 6, 9])  # one group of four queries per workgroup / eight (6 used) / 8 + 1
 def test_index_full_multiquery_causal_ratio2(csa, orc, nq):
     B, E, ratio = 2, 5000, 2
