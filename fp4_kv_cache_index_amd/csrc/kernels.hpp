@@ -39,6 +39,7 @@ struct IndexWs {
   uint64_t* cand;   // [BQ][2][8192] candidate u64 keys
   uint32_t* keys;   // [BQ][slots] score key of every entry (Full) or pool slot (Reindex)
   uint32_t* bkeys;  // [BQ][slots / 8] block-maximum keys (Full with a pool)
+  int32_t* bound;   // [BQ][2][4] boundary bin, keys above it, all keys (written by the filter)
   int64_t slots;
 };
 int64_t index_slots(int32_t capacity);
