@@ -199,3 +199,26 @@ def test_debug_flags_short_window_length(csa):
         assert probe(csa) == csa.OK
         r2 = host(ring2)
         assert np.array_equal(r2, r)  # the same single token in slot 0
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])  # 16 x 128K, 4 x 1M, 16 x 128K with six queries
+def test_debug_full_size_step_matches_release(csa, cid):
+    """A whole group step at full size through the debug library records no
+    violation and gives the release library's outputs and cache bytes."""
+    import bench
+    wl = bench.Workload(cid, replicas=2, extra_steps=4)  # two identical cache replicas
+    wl.inputs[1] = wl.inputs[0]
+    wl.step(0)
+    torch.cuda.synchronize()
+    rel = [t.clone() for t in wl.topk] + [wl.pool.clone()] + [o.clone() for o in wl.out]
+    with csa.using(csa.debug_lib()):
+        wl.step(1)
+        torch.cuda.synchronize()
+        assert probe(csa) == csa.OK
+    dbg = list(wl.topk) + [wl.pool] + list(wl.out)
+    for i, (a, b) in enumerate(zip(rel, dbg)):
+        assert torch.equal(a, b), i
+    for name in ("kv_codes", "kv_scales", "ik_codes", "ik_scales", "length"):
+        assert torch.equal(getattr(wl.caches[0], name), getattr(wl.caches[1], name)), name
+    for l in range(wl.L):
+        assert torch.equal(wl.swas[0][l], wl.swas[1][l]), l
