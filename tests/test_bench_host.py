@@ -1,0 +1,88 @@
+"""Host-side logic of bench.py that needs no GPU: it refuses more than one GPU,
+reports HBM traffic only while the counter record matches the kernel source,
+and turns the rocprofv3 counter CSVs into bytes per launch."""
+import json
+import os
+import subprocess
+import sys
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout
+
+
+def test_percentiles():
+    import bench
+    assert bench.pct([1.0, 2.0, 3.0, 4.0, 5.0]) == [1.4, 3.0, 4.6]
+
+
+def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
+    """The committed record's hash matches index.hip as it is, so its bytes are
+    reported; once the source differs the figure is withheld (None)."""
+    import bench
+
+    class W:
+        name = "f_ri_2ru_b16_ctx128k"
+
+    rec = json.load(open(os.path.join(ROOT, "profiles", "counters_index_full_f_ri_2ru_b16_ctx128k.json")))
+    assert bench.traffic_from_profiles(W, "index_full") == rec["hbm_bytes_per_launch"]
+    # a copy of the tree whose index.hip differs by one byte
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "profiles" / "counters_index_full_f_ri_2ru_b16_ctx128k.json").write_text(json.dumps(rec))
+    src = open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", "index.hip"), "rb").read()
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index.hip").write_bytes(src + b"\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.traffic_from_profiles(W, "index_full") is None
+
+    class Other:
+        name = "no_such_workload"
+
+    assert bench.traffic_from_profiles(Other, "index_full") is None
+
+
+def test_counter_summary(tmp_path, monkeypatch):
+    """Two synthetic counter CSVs: the last three device copies fix the scale
+    factors, the Full call's final kernel is the one with the larger grid (it
+    also builds the pool), and each kernel's mean per dispatch is scaled."""
+    import bench
+    fields = "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+
+    def rows(counter, values):
+        return fields + "".join(f'{i},"{k}",{g},{counter},{v}\n' for i, (k, g, v) in enumerate(values))
+
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [(copy, 4096, 999.0),  # an earlier copy: not a calibration copy
+             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 70000.0),
+             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 70002.0),
+             ("csa2::index_filter_kernel(...)", 131072, 5000.0),
+             ("csa2::index_final_kernel(...)", 16384, 600.0),     # the Full call's (kinds x queries)
+             ("csa2::index_final_kernel(...)", 8192, 12345.0),    # a Reindex call's: left out
+             ("void csa2::index_score_kernel<1024, true>(...)", 131072, 777.0),
+             (copy, 65536, 131072.0), (copy, 65536, 131072.0), (copy, 65536, 131072.0)]
+    write = [(copy, 4096, 999.0),
+             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 9500.0),
+             ("csa2::index_filter_kernel(...)", 131072, 600.0),
+             ("csa2::index_final_kernel(...)", 16384, 1600.0),
+             ("csa2::index_final_kernel(...)", 8192, 54321.0),
+             (copy, 65536, 262144.0), (copy, 65536, 262144.0), (copy, 65536, 262144.0)]
+    f = tmp_path / "fetch.csv"
+    w = tmp_path / "write.csv"
+    f.write_text(rows("FETCH_SIZE", fetch))
+    w.write_text(rows("WRITE_SIZE", write))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index.hip").write_bytes(b"// source\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    bench.summarize_counters(str(f), str(w), "wl_test")
+    out = json.load(open(tmp_path / "profiles" / "counters_index_full_wl_test.json"))
+    assert abs(out["fetch_factor"] - 2.0) < 1e-12 and abs(out["write_factor"] - 1.0) < 1e-12
+    assert out["fetch_kib_score"] == 70001.0 and out["fetch_kib_final"] == 600.0
+    want = ((70001.0 + 5000.0 + 600.0) * 2.0 + (9500.0 + 600.0 + 1600.0)) * 1024
+    assert out["hbm_bytes_per_launch"] == round(want)
+    assert out["source"] == "index.hip" and len(out["source_sha256"]) == 64
