@@ -621,8 +621,8 @@ def main():
         summarize_counters(*args.summarize_counters, synth.WORKLOADS[args.config]["name"])
         return
     if args.gpus != 1:
-        print(f"bench.py: this build targets one GPU; --gpus {args.gpus} is not supported "
-              "(sharding across GPUs is described, not built)", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(it is not sharded across GPUs)", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: run one process on one GPU", file=sys.stderr)
