@@ -499,7 +499,20 @@ def cpu_baseline(wl, steps=2):
         log(f"oracle step {s_i}: {times[-1]:.2f}s")
     t_step = float(np.median(times))
     value = wl.L / t_step * ost.hs / wl.B
-    return dict(value=value, unit=UNIT, cores=int(min(ost.orc.num_threads(), ost.hs * wl.Q)), kind="oracle",
+    cores = int(min(ost.orc.num_threads(), ost.hs * wl.Q))
+    # one more step on a single thread, for the per-core rate, when it should
+    # take well under a minute
+    single = None
+    n_thr = ost.orc.num_threads()
+    if t_step * cores <= 40.0:
+        ost.orc.set_threads(1)
+        t = time.time()
+        ost.step()
+        t_one = time.time() - t
+        ost.orc.set_threads(n_thr)
+        single = wl.L / t_one * ost.hs / wl.B
+        log(f"oracle step on one thread: {t_one:.2f}s")
+    return dict(value=value, unit=UNIT, cores=cores, kind="oracle", single_thread_value=single,
                 cpu_model=cpu_model(),
                 sample=f"{steps} group steps of the first {ost.hs} of {wl.B} sequences (full context, all {wl.L} "
                        f"layers), median {t_step:.2f}s per step, scaled by {wl.B}/{ost.hs} to the whole batch")

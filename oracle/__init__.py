@@ -85,6 +85,8 @@ def _declare(L):
     L.orc_attend.argtypes = [u8p, u8p, i32p, i32, i32, i32, i32p, u8p, i32, f32p, i32p, ctypes.c_float,
                              f64p, f64p, i32]
     L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_threads.restype = None
+    L.orc_set_threads.argtypes = [ctypes.c_int]
 
 
 def _p(a, ct):
@@ -310,3 +312,9 @@ def attend(cache: Cache, topk, swa, q, sm_scale, q_pos=None):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops (timing only: results do not
+    depend on the count)."""
+    lib().orc_set_threads(int(n))
