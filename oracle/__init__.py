@@ -71,6 +71,7 @@ def _declare(L):
     L.orc_dequant_main_rows.argtypes = [u8p, u8p, i64, f64p]
     L.orc_quantize_ik_rows.argtypes = [f32p, i64, u8p, f32p]
     L.orc_compress_pairs.argtypes = [f32p, f32p, i64, f32p]
+    L.orc_compress.argtypes = [f32p, f32p, ctypes.c_int32, i64, f32p]
     L.orc_quantize_query.argtypes = [f32p, u8p, f32p]
     L.orc_entry_score.restype = ctypes.c_float
     L.orc_entry_score.argtypes = [u8p, f32p, f32p, u8p, ctypes.c_float]
@@ -195,6 +196,18 @@ def compress_pairs(x, z):
     return out
 
 
+def compress(x, z, m):
+    """[m n][512] tokens + logits -> [n][512] fp32 entries: the ratio-2 rule
+    over m consecutive tokens (per-channel softmax of the logits weighting the
+    values, fp64 sums in token order, one rounding)."""
+    x = _c(x, np.float32)
+    z = _c(z, np.float32)
+    n = x.shape[0] // m
+    out = np.empty((n, D), np.float32)
+    lib().orc_compress(_p(x, ctypes.c_float), _p(z, ctypes.c_float), int(m), n, _p(out, ctypes.c_float))
+    return out
+
+
 def project_ik(entries, w_ik):
     """Indexer K derived from main-KV entries (ai.info "Methodology in Plain
     English": CSA2 takes indexer K from a projection of the main KV entries).
@@ -251,11 +264,14 @@ def quantize_append(cache: Cache, kv, ik, logits=None):
 
 def quantize_append_proj(cache: Cache, kv, w_ik, logits=None):
     """quantize_append with each new entry's indexer K = project_ik(entry), the
-    entry being the token row (ratio 1) or the compressed pair (ratio 2)."""
+    entry being the token row (ratio 1) or the tokens it compresses (ratio 2 or more)."""
     kv = _c(kv, np.float32)
     if cache.ratio == 2:
         logits = _c(logits, np.float32)
         entries = np.stack([compress_pairs(kv[b], logits[b]) for b in range(kv.shape[0])])
+    elif cache.ratio > 2:
+        logits = _c(logits, np.float32)
+        entries = np.stack([compress(kv[b], logits[b], cache.ratio) for b in range(kv.shape[0])])
     else:
         entries = kv
     quantize_append(cache, kv, project_ik(entries, w_ik), logits=logits)
