@@ -10,13 +10,14 @@
 namespace {
 
 constexpr int64_t kMaxCapacity = 2048LL * csa2::kFullChunk;  // chunk lists one merge accepts
+constexpr int32_t kMaxRatio = 16;                              // tokens per compressed entry
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int check_cache(const csa2_cache* c, bool need_index, bool need_main) {
   if (!c) return CSA2_EINVAL;
   if (c->batch < 0 || c->capacity < 0) return CSA2_EINVAL;
-  if (c->ratio != 1 && c->ratio != 2) return CSA2_EINVAL;
+  if (c->ratio < 1 || c->ratio > kMaxRatio) return CSA2_EINVAL;
   if (c->capacity > kMaxCapacity) return CSA2_EUNSUPPORTED;
   if (c->batch == 0) return CSA2_OK;
   if (!c->length || !aligned(c->length, 4)) return CSA2_EINVAL;
@@ -64,7 +65,7 @@ static int quantize_append_impl(const csa2_cache* cache, const float* kv, const 
   if (rc != CSA2_OK) return rc;
   if (T < 0 || host_len_bound < 0) return CSA2_EINVAL;
   if (T % cache->ratio != 0) return CSA2_EINVAL;
-  if ((cache->ratio == 2) != (logits != nullptr)) return CSA2_EINVAL;
+  if ((cache->ratio >= 2) != (logits != nullptr)) return CSA2_EINVAL;
   const int64_t n_new = T / cache->ratio;
   if ((int64_t)host_len_bound + n_new > cache->capacity) return CSA2_ECAPACITY;
   if (cache->batch == 0 || T == 0) return CSA2_OK;

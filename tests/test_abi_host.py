@@ -85,7 +85,10 @@ def test_append_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     q = L.csa2_quantize_append
     assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
-    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL   # T % r
+    assert q(ctypes.byref(cache(csa, ratio=0)), p, p, p, 1, 0, None) == csa.EINVAL      # ratio 1..16
+    assert q(ctypes.byref(cache(csa, ratio=17)), p, p, p, 17, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=4)), p, None, p, 4, 0, None) == csa.EINVAL   # logits missing
     assert q(ctypes.byref(cache(csa, ratio=2)), p, p, p, 3, 0, None) == csa.EINVAL      # T % r
     assert q(ctypes.byref(cache(csa, ratio=2)), p, None, p, 2, 0, None) == csa.EINVAL   # logits missing
     assert q(ctypes.byref(cache(csa, ratio=1)), p, p, p, 2, 0, None) == csa.EINVAL      # logits given
@@ -102,7 +105,10 @@ def test_append_proj_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     q = L.csa2_quantize_append_proj
     assert q(None, p, None, p, 1, 0, None) == csa.EINVAL
-    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=3)), p, None, p, 1, 0, None) == csa.EINVAL   # T % r
+    assert q(ctypes.byref(cache(csa, ratio=0)), p, p, p, 1, 0, None) == csa.EINVAL      # ratio 1..16
+    assert q(ctypes.byref(cache(csa, ratio=17)), p, p, p, 17, 0, None) == csa.EINVAL
+    assert q(ctypes.byref(cache(csa, ratio=4)), p, None, p, 4, 0, None) == csa.EINVAL   # logits missing
     assert q(ctypes.byref(cache(csa, ratio=2)), p, p, p, 3, 0, None) == csa.EINVAL      # T % r
     assert q(ctypes.byref(cache(csa, ratio=2)), p, None, p, 2, 0, None) == csa.EINVAL   # logits missing
     assert q(ctypes.byref(cache(csa, cap=10)), p, None, p, 4, 7, None) == csa.ECAPACITY

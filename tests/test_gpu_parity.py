@@ -62,14 +62,16 @@ def special_rows(n):
 
 # ------------------------------------------------------------------ append
 @pytest.mark.parametrize("B,T,ratio,pre", [(1, 1, 1, 0), (3, 5, 1, 7), (2, 64, 1, 0), (1, 300, 1, 5),
-                                           (2, 8, 2, 3), (1, 2048, 2, 0)])
+                                           (2, 8, 2, 3), (1, 2048, 2, 0),
+                                           # ratio m above 2: the same rule over m tokens
+                                           (2, 12, 3, 1), (1, 64, 4, 0), (2, 40, 8, 2), (1, 512, 16, 0)])
 def test_quantize_append_bitexact(csa, orc, B, T, ratio, pre):
     n_new = T // ratio
     cap = pre + n_new + 3
     kv = special_rows(B * T).reshape(B, T, 512)
     ik = synth.normal(12, f"ik{T}", (B, n_new, 64)) * np.float32(3.0)
     ik[0, 0] = 0.0
-    logits = synth.normal(12, f"lg{T}", (B, T, 512)) * np.float32(2.0) if ratio == 2 else None
+    logits = synth.normal(12, f"lg{T}", (B, T, 512)) * np.float32(2.0) if ratio >= 2 else None
     oc = orc.Cache(B, cap, ratio)
     oc.length[:] = pre
     orc.quantize_append(oc, kv, ik, logits=logits)
@@ -90,6 +92,8 @@ def test_quantize_append_bitexact(csa, orc, B, T, ratio, pre):
     (2, 600, 1),     # several workgroups per sequence, second launch advances the lengths
     (2, 2, 2),       # one compressed pair
     (1, 1030, 2),    # 515 compressed entries
+    (2, 12, 3),      # ratio 3
+    (1, 256, 4),     # 64 entries of four tokens
 ])
 def test_quantize_append_proj_bitexact(csa, orc, B, T, ratio):
     """Indexer K projected from each entry (w_ik [512][64]): every cache byte
@@ -104,7 +108,7 @@ def test_quantize_append_proj_bitexact(csa, orc, B, T, ratio):
     gc.host_len_bound = 2
     for call in range(2):
         kv = special_rows(B * T).reshape(B, T, 512) if call == 0 else synth.normal(13, f"kv{T}", (B, T, 512))
-        logits = synth.normal(13, f"lg{T}_{call}", (B, T, 512)) * np.float32(2.0) if ratio == 2 else None
+        logits = synth.normal(13, f"lg{T}_{call}", (B, T, 512)) * np.float32(2.0) if ratio >= 2 else None
         orc.quantize_append_proj(oc, kv, w, logits=logits)
         csa.quantize_append_proj(gc, dev(kv), dev(w), logits=dev(logits) if logits is not None else None)
         assert np.array_equal(host(gc.length), oc.length)
@@ -218,6 +222,39 @@ def test_index_empty_sequences(csa, orc, Q):
     rt = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
     csa.index_score_topk(gc, csa.REINDEX, dev(iq), rt, q_pos=dev(q_pos), pool_in=dev(empty))
     assert (host(rt) == -1).all()
+
+
+def test_index_and_attend_ratio4(csa, orc):
+    """Entries of four tokens: visibility (e + 1) * 4 - 1 <= p for three
+    consecutive queries, Full Top-K and pool, and attention over them."""
+    B, r, Q = 2, 4, 3
+    lengths = [3000, 1200]
+    cap = 3010
+    oc = oracle_cache_full(orc, B, cap, lengths, 27, ratio=r)
+    last = np.array([lengths[0] * r - 1, lengths[1] * r - 7], np.int64)  # the second ends mid-entry
+    q_pos = (last[:, None] - (Q - 1) + np.arange(Q)[None, :]).astype(np.int32)
+    iq = synth.normal(27, "iq", (B, Q, 4, 64))
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_pool=True, want_scores=True)
+    gc = upload(csa, oc, with_main=True)
+    topk, pool = run_full(csa, gc, iq, q_pos=q_pos)
+    for b in range(B):
+        for q in range(Q):
+            n_vis = min(lengths[b], (int(q_pos[b, q]) + 1) // r)
+            topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"b{b} q{q}")
+            pool_block_swaps(pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
+    S = 128 + Q
+    swa = np.zeros((B, S, 512), np.uint8)
+    for b in range(B):
+        n_tok = int(last[b]) + 1
+        x = synth.normal_rows(27, "swa", b * 100000 + n_tok - S, S, 512).reshape(1, S, 512)
+        sub = np.zeros((1, S, 512), np.uint8)
+        orc.swa_append(sub, x, np.array([n_tok], np.int32))
+        swa[b] = sub[0]
+    qf = bf16_round(synth.normal(27, "q", (B, Q, 16, 512)))
+    ref, _ = orc.attend(oc, topk, swa, qf.float().numpy(), SM, q_pos=q_pos)
+    out = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out, SM, q_pos=dev(q_pos))
+    attn_close(host(out.float()), ref, name="attend ratio 4")
 
 
 @pytest.mark.parametrize("nq", [4, 6, 9])  # one group of four queries per workgroup / eight (6 used) / 8 + 1
