@@ -49,3 +49,39 @@ def test_graph_replays_match_eager_steps(csa, cid):
         for l in range(wl.L):
             assert torch.equal(wl.swas[0][l], wl.swas[1][l]), f"replay {rep}: window of layer {l}"
         print(f"config {cid}: replay {rep} equals the eager step", flush=True)
+
+
+@pytest.mark.parametrize("B,ctx", [(4, 16384), (16, 131072)])
+def test_schedule38_graph_replays_match_eager_steps(csa, B, ctx):
+    """The same check for the whole 38-layer schedule (two tokens per step,
+    projected appends into three ratio-2 encoder caches and the decoder cache)."""
+    import bench
+    wl = bench.Schedule38(6, B, ctx, 2)
+    wl.inputs[1] = wl.inputs[0]
+    wl.step(0)
+    wl.step(1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wl.step(1)
+    torch.cuda.synchronize()
+
+    def outputs():
+        outs = [o for per_t in wl.out for o in per_t]
+        return outs + [wl.topk[k] for k in sorted(wl.topk)] + [wl.pool]
+
+    for rep in range(3):
+        wl.step(0)
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in outputs()]
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(eager, outputs())):
+            assert torch.equal(a, b), f"replay {rep}: output {i}"
+        for n in wl.caches[0]:
+            for name in ("kv_codes", "kv_scales", "ik_codes", "ik_scales", "length"):
+                assert torch.equal(getattr(wl.caches[0][n], name), getattr(wl.caches[1][n], name)), \
+                    f"replay {rep}: cache {n} {name}"
+        for l in range(len(wl.swas[0])):
+            assert torch.equal(wl.swas[0][l], wl.swas[1][l]), f"replay {rep}: window of layer {l}"
+        print(f"schedule {B} x {ctx}: replay {rep} equals the eager step", flush=True)
