@@ -222,3 +222,28 @@ def test_debug_full_size_step_matches_release(csa, cid):
         assert torch.equal(getattr(wl.caches[0], name), getattr(wl.caches[1], name)), name
     for l in range(wl.L):
         assert torch.equal(wl.swas[0][l], wl.swas[1][l]), l
+
+
+def test_debug_schedule_step_matches_release(csa):
+    """The whole 38-layer schedule (ratio-2 encoder caches, two tokens per step,
+    explicit positions, projected appends) through the debug library: nothing
+    recorded, the release library's outputs and caches byte for byte."""
+    import bench
+    wl = bench.Schedule38(6, 4, 16384, 2)
+    wl.inputs[1] = wl.inputs[0]
+
+    def outputs():
+        return [o for per_t in wl.out for o in per_t] + [wl.topk[k] for k in sorted(wl.topk)] + [wl.pool]
+
+    wl.step(0)
+    torch.cuda.synchronize()
+    rel = [t.clone() for t in outputs()]
+    with csa.using(csa.debug_lib()):
+        wl.step(1)
+        torch.cuda.synchronize()
+        assert probe(csa) == csa.OK
+    for i, (a, b) in enumerate(zip(rel, outputs())):
+        assert torch.equal(a, b), i
+    for n in wl.caches[0]:
+        for name in ("kv_codes", "kv_scales", "ik_codes", "ik_scales", "length"):
+            assert torch.equal(getattr(wl.caches[0][n], name), getattr(wl.caches[1][n], name)), (n, name)
