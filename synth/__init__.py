@@ -86,7 +86,10 @@ def torch_normal_rows(config_id: int, tag: str, row0: int, n_rows: int, width: i
     """Rows [row0, row0 + n_rows) of an endless N(0, 1) fp32 matrix drawn on the
     device with torch's generator, seeded per 65,536-row chunk like normal_rows.
     Same recipe, different stream of numbers: both sides of a comparison must use
-    the same function (the host side copies the device rows)."""
+    the same function (the host side copies the device rows).  torch's normal
+    draws are not prefix-consistent across draw sizes, so a row range is
+    reproduced by the same call, or as part of a whole chunk, not by drawing a
+    sub-range alone."""
     import torch
     out = torch.empty((n_rows, width), dtype=torch.float32, device=device)
     r = row0
