@@ -134,3 +134,51 @@ def test_random_case(csa, orc, case):
     csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out, SM, q_pos=dev(att_pos))
     mabs, _ = attn_close(host(out.float()), ref, name=f"case {case} attend")
     print(f"case {case}: ok, attention max abs err {mabs:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_ratio_m_case(csa, orc, case):
+    """Ratios above 2 end to end: the cache is built by the compressing append
+    from token rows and logits (bytes compared with the oracle's), then Full
+    scoring with a pool and attention run over it."""
+    g = synth.generator(CID, "rcase", case)
+    m = int(g.choice([3, 4, 8]))
+    B = int(g.integers(1, 4))
+    Q = int(g.choice([1, 2, 5, 8]))
+    n = int(g.integers(200, 3000))
+    T, cap = n * m, n + int(g.integers(0, 40))
+    print(f"ratio case {case}: m={m} B={B} Q={Q} entries={n} cap={cap}", flush=True)
+    kv = synth.normal_rows(CID, f"rkv{case}", 0, B * T, 512).reshape(B, T, 512)
+    lg = synth.normal_rows(CID, f"rlg{case}", 0, B * T, 512).reshape(B, T, 512)
+    ik = synth.normal_rows(CID, f"rik{case}", 0, B * n, 64).reshape(B, n, 64)
+    oc = orc.Cache(B, cap, m)
+    orc.quantize_append(oc, kv, ik, logits=lg)
+    gc = csa.Cache(B, cap, m)
+    csa.quantize_append(gc, dev(kv), dev(ik), logits=dev(lg))
+    for name in ("kv_codes", "kv_scales", "ik_codes", "length"):
+        assert np.array_equal(host(getattr(gc, name)), getattr(oc, name)), name
+    assert np.array_equal(host(gc.ik_scales).view(np.uint32), oc.ik_scales.view(np.uint32))
+
+    iq = synth.normal(CID, f"riq{case}", (B, Q, 4, 64))
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+    topk = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
+    pool = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.FULL, dev(iq), topk, pool_out=pool)
+    topk, g_pool = host(topk), host(pool)
+    pos = n * m - Q + np.arange(Q)  # the last Q tokens (the default positions)
+    for b in range(B):
+        for q in range(Q):
+            n_vis = min(n, (int(pos[q]) + 1) // m)
+            topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"ratio case {case} b{b} q{q}")
+            pool_block_swaps(g_pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"ratio case {case} pool")
+
+    S = 128 + Q
+    swa = np.zeros((B, S, 512), np.uint8)
+    x = synth.normal_rows(CID, f"rswa{case}", 0, B * S, 512).reshape(B, S, 512)
+    orc.swa_append(swa, x, np.full(B, n * m, np.int32))
+    qf = torch.from_numpy(synth.normal(CID, f"rq{case}", (B, Q, 16, 512))).to(torch.bfloat16)
+    ref, _ = orc.attend(oc, topk, swa, qf.float().numpy(), SM)
+    out = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out, SM)
+    mabs, _ = attn_close(host(out.float()), ref, name=f"ratio case {case} attend")
+    print(f"ratio case {case}: ok, attention max abs err {mabs:.2e}", flush=True)
