@@ -6,29 +6,36 @@
 // Optionally the same launch first appends the layer's new window tokens.
 //
 // Key slots per query: 0..511 = the Top-512 list, 512..639 = window positions
-// p-127..p.  A workgroup (4 waves) walks a range of slots in tiles of 32:
-//   gather: thread (kg, grp) owns keys 4kg..4kg+3 of the tile and channels
-//     16grp..16grp+15, i.e. one E4M3 scale group per key (8 code bytes + 1
-//     scale byte, or 16 window bytes);
-//   dequantise: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the E2M1 values
-//     exactly and one v_pk_mul_f16 by the group scale gives x = code * scale,
-//     exact in fp16 (at most 6 significant bits, |x| in [2^-10, 2688]); window
-//     bytes widen exactly with v_cvt_scalef32_pk_f16_fp8.  The tile lands in
-//     LDS once, as fp16 [key][dim];
-//   S = Q K^T on v_mfma_f32_16x16x32_f16: the bf16 query is scaled per head by
-//     a power of two that puts its largest element in [2^14, 2^15), which makes
-//     the fp16 copy exact for every element within 2^-28 of the head's largest,
-//     and the scores are scaled back exactly (16 heads = the 16 MFMA rows; wave
-//     w covers dims 128w..128w+127 and the four partial S are summed in LDS);
-//   online softmax in fp32 (running max and sum per head);
-//   O += P V on v_mfma_f32_16x16x32_f16, wave w owning output dims 128w..; the
-//     V operand (8 keys of one dim per lane) comes straight from the [key][dim]
-//     tile through the LDS transpose read ds_read_b64_tr_b16.
-// With several splits per query the unnormalised partials (O, max, sum) go to
-// the workspace and a second kernel merges them by log-sum-exp weights, one
-// workgroup per (query, head).  (Merging in the last workgroup of each query
-// needs a device-scope release per workgroup, an L2 write-back that costs more
-// on gfx950 than the second launch.)
+// p-127..p, taken in groups of 16.  A workgroup of four waves owns a range of
+// groups (a split); every wave runs its own groups start to finish, so the
+// key loop has no workgroup barrier:
+//   gather: lane l holds key l%16 of the group, channels 128(l/16)..+127
+//     (64 FP4 code bytes and 8 E4M3 scale bytes of a main row, or 128 bytes of
+//     a window row), as raw buffer loads issued one group ahead;
+//   dequantise in registers: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the
+//     E2M1 values exactly and one fp16 multiply by the group scale gives
+//     x = code * scale, exact in fp16 (at most 6 significant bits, |x| in
+//     [2^-10, 2688]); window bytes widen exactly with v_cvt_scalef32_pk_f16_fp8;
+//   S^T = K Q^T on v_mfma_f32_16x16x32_f16 straight from those registers (key
+//     rows are the matrix rows, the 16 heads its columns; the contraction
+//     order of the 512 channels is permuted identically on both operands).
+//     The bf16 query is scaled per head by a power of two that puts its
+//     largest element in [2^14, 2^15), which makes its fp16 copy exact for
+//     every element within 2^-28 of the head's largest; the scores are scaled
+//     back exactly;
+//   softmax in fp32: lane l holds head l%16 for keys 4(l/16)..+3, which is
+//     the layout of the P^T operand of the next product, so P never leaves
+//     registers, and the running max, sum and rescaling are per lane;
+//   O^T += V^T P^T on v_mfma_f32_16x16x16_f16: the dequantised group goes to a
+//     per-wave LDS tile [key][channel] and comes back channel-major through
+//     the transposing read ds_read_b64_tr_b16.  O^T keeps head l%16 in lane l.
+// At the end the four waves' (max, sum, O) are combined through LDS.  With
+// one split the workgroup writes the bf16 output; with several it writes its
+// unnormalised fp32 partial and a second kernel merges the splits by their
+// maxima.  (Merging inside the launch would need the partials visible across
+// the XCDs' separate L2 caches: an agent-scope release writes back the L2 and
+// measured 40-90 us per launch on gfx950, against 1.9 us for a dependent
+// launch.)
 #include <hip/hip_runtime.h>
 
 #include "block_ops.hpp"
@@ -40,48 +47,38 @@ namespace csa2 {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-
-// LDS transpose read: in each 16-lane group, lane 4j+q names 4 consecutive fp16
-// of row j; lane i receives element i%4 of lanes i/4, i/4+4, i/4+8, i/4+12,
-// i.e. column i of the 4-row block.
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4h lds_read_tr16(const _Float16* p) {
-  return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
-}
 
-constexpr int kThreads = 256;
-constexpr int kKStride = 528;  // fp16 per key row of the [key][dim] tile (512 + pad)
-constexpr int kPStride = 40;
-constexpr int kRedStride = 80;  // 64 lanes + pad: the four row groups start 16 banks apart
-constexpr int kTilesPerQuery = kAttnKeys / kAttnTile;  // 20
-constexpr int kMaxSplits = 10;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeyGroup = 16;                      // keys per group (one MFMA tile of keys)
+constexpr int kMainGroups = 512 / kKeyGroup;       // groups 0..31 hold Top-K slots, 32..39 the window
+constexpr int kVStride = 528;                      // fp16 per key row of a wave's V tile (512 + pad)
+constexpr int kQStride = 520;                      // fp16 per head row of the scaled query (512 + pad)
+constexpr int kXStride = 260;                      // fp32 per head row of the final exchange (256 + pad)
 constexpr int kFusedAppendMax = 8;  // new window tokens per sequence appended inside the attention launch
+static_assert(kWaves * 16 * kXStride * 4 <= kWaves * 16 * kVStride * 2, "exchange fits in the V tiles");
 
-// Splits per query, at most kMaxSplits, rounded so every split holds as many
-// tiles.  At most one workgroup per compute unit while that still gives four
-// or more splits: workgroups sharing a compute unit mostly queue behind each
-// other (measured: 32 queries run best as 7 splits, not 10).  Fewer queries
-// than that get about two workgroups per compute unit instead (96 queries: 5
-// splits beat 2, 3 and 10).
+// Splits per query (each a workgroup of four waves; groups per wave = 10 /
+// splits).  Few queries spread every query over 10 workgroups of one group per
+// wave, so that each workgroup gathers only 64 rows: a gather's time grows with
+// the rows one compute unit fetches (measured on gfx950, 10,240 rows: 2.8 us at
+// 16 rows per workgroup, 4.0 at 64, 6.2 at 128).  Many queries fill the chip
+// with fewer splits and need no merge at all from 1,024 queries on.
 int attend_splits(int64_t bq) {
-  int64_t s = 256 / bq;
-  if (s < 4) s = (512 + bq - 1) / bq;
-  if (s < 1) s = 1;
-  if (s > kMaxSplits) s = kMaxSplits;
-  const int tps = (int)((kTilesPerQuery + s - 1) / s);
-  return (kTilesPerQuery + tps - 1) / tps;
+  if (bq <= 64) return 10;
+  if (bq <= 256) return 5;
+  if (bq <= 1024) return 2;
+  return 1;
 }
 
-static inline int tiles_per_split(int splits) { return (kTilesPerQuery + splits - 1) / splits; }
-
-// [partial O, normalised by its own sum: splits x bq x 16 x 512 fp16]
-// [partial (max, sum): splits x bq x 16 x 2 f32]
+// [partial O, unnormalised fp32: splits x bq x 16 x 512] [partial (max, sum): splits x bq x 16 x 2 f32]
 size_t attend_ws_bytes(int64_t bq) {
   const int s = attend_splits(bq);
   if (s == 1) return 0;
-  return 256 + (size_t)s * bq * (16 * 512 * 2 + 16 * 2 * 4);
+  return 256 + (size_t)s * bq * (16 * 512 * 4 + 16 * 2 * 4);
 }
 
 struct AttnArgs {
@@ -99,10 +96,10 @@ struct AttnArgs {
   const int32_t* q_pos;
   float sm_scale;
   int32_t Q;
-  int32_t tps, splits;
+  int32_t splits;
   uint16_t* out;
   float* lse;
-  _Float16* part_o;
+  float* part_o;
   float* part_ml;
   int64_t bq_total;
 };
@@ -115,391 +112,568 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 
 __device__ __forceinline__ uint32_t h2_bits(v2h h) { return __builtin_bit_cast(uint32_t, h); }
 
-// A raw buffer of `bytes` bytes at p: a load past the end returns zeros without
-// a memory access, so a load that may not be wanted needs no branch around it
-// (the compiler waits for a load under a branch before the branch ends).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+// A raw buffer of `bytes` bytes at p: a load at an offset past the end returns
+// zeros without a memory access, so a load that may not be wanted is issued
+// anyway, with no branch around it (the compiler waits for a load under a
+// branch before the branch ends).
+__device__ __forceinline__ BufRsrc make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOff = 0x80000000u;  // an offset past every buffer here
+
+__device__ __forceinline__ uint4 buf16(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// LDS transpose read: in each 16-lane group, lane 4j+q names 4 consecutive fp16
+// of row j; lane i receives element i%4 of lanes i/4, i/4+4, i/4+8, i/4+12,
+// i.e. column i of the 4-row block.
+__device__ __forceinline__ v4h lds_read_tr16(const _Float16* p) {
+  return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p)));
+}
+
+// LDS ordering inside one wave: the wave's earlier LDS stores are complete and
+// visible to all of its lanes, and the compiler moves no LDS access across.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// max / sum of one value per lane over the four lanes l%16 + 16j (the four
+// rows of a wave), every lane getting the result
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // 8 E2M1 codes (low nibble first) times a group scale, as four fp16x2 words
-__device__ __forceinline__ void fp4_group(uint32_t w, v2h s2, uint32_t* o) {
+__device__ __forceinline__ void fp4_word(uint32_t w, v2h s2, uint32_t* o) {
   o[0] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
   o[1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
   o[2] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
   o[3] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
 }
 
-template <bool kRefill>
-__global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[kAttnTile * kKStride];
-  __shared__ float s_red[4][2][4][kRedStride];  // [wave][key block][row group i][lane]
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[16 * kPStride];
-  __shared__ float s_m[16], s_l[16], s_alpha[16];
-  __shared__ float s_qmax[4][16];
-  __shared__ float s_qfac[16];
-  __shared__ int s_valid[kAttnTile];
-  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
-  __shared__ __attribute__((aligned(16))) int32_t s_ids[512];                     // the query's Top-K row
+// One group's raw bytes for this lane, as loaded: w[0..7] 128 bytes (a main row
+// uses w[0..3], its 64 code bytes), sc the 8 scale bytes of a main row.
+struct Raw {
+  uint4 w[8];
+  uint2 sc;
+};
 
+// What a workgroup knows about its (query, split).
+struct Wg {
+  int64_t bq;
+  int split, b, qi, tid, wave, n, g;  // n = lane % 16 (key row of S^T, head column), g = lane / 16
+  int32_t p;                          // the query's token position
+  int32_t new_lo, new_hi;             // new window tokens: positions new_lo .. new_hi-1
+  int32_t n_vis_dbg;                  // debug builds: entries the query may list
+  bool stage;                         // stages the new window tokens (holds window groups)
+  int first_win_split;
+  BufRsrc ids_r, codes_r, scales_r, swa_r, none_r;
+};
+
+__device__ __forceinline__ Wg make_wg(const AttnArgs& a, int gpw) {
+  Wg w;
   const int64_t wr = xcd_rank(blockIdx.x, (int64_t)a.splits * a.bq_total);
-  const int split = (int)(wr % a.splits);
-  const int64_t bq = wr / a.splits;
-  const int Q = a.Q;
-  const int b = (int)(bq / Q), qi = (int)(bq % Q);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t p = a.q_pos ? a.q_pos[bq] : a.length[b] * a.ratio - Q + qi;
-  // new window tokens are positions new_lo .. new_hi-1
-  const int32_t new_hi = a.swa_x ? a.swa_len[b] : 0;
-  const int32_t new_lo = a.swa_x ? new_hi - a.swa_T : 0;
-  // debug builds: the entries this query may list; a listed id at or past them
-  // is flagged and skipped
-  int32_t n_vis_dbg = 0;
+  w.split = (int)(wr % a.splits);
+  w.bq = wr / a.splits;
+  w.b = (int)(w.bq / a.Q);
+  w.qi = (int)(w.bq % a.Q);
+  w.tid = threadIdx.x;
+  w.wave = w.tid >> 6;
+  w.n = w.tid & 15;
+  w.g = (w.tid & 63) >> 4;
+  w.p = a.q_pos ? a.q_pos[w.bq] : a.length[w.b] * a.ratio - a.Q + w.qi;
+  w.new_hi = a.swa_x ? a.swa_len[w.b] : 0;
+  w.new_lo = a.swa_x ? w.new_hi - a.swa_T : 0;
+  w.n_vis_dbg = 0;
   if (kDebug) {
-    const int32_t len = a.length[b];
-    if (tid == 0 && split == 0 && (len < 0 || len > a.cap)) dev_flag(kErrLength);
-    if (tid == 0 && split == 0 && new_lo < 0) dev_flag(kErrSeqLen);
-    const int64_t by_pos = p < 0 ? 0 : ((int64_t)p + 1) / a.ratio;
-    n_vis_dbg = (int32_t)min((int64_t)min(len, a.cap), by_pos);
+    const int32_t len = a.length[w.b];
+    if (w.tid == 0 && w.split == 0 && (len < 0 || len > a.cap)) dev_flag(kErrLength);
+    if (w.tid == 0 && w.split == 0 && w.new_lo < 0) dev_flag(kErrSeqLen);
+    const int64_t by_pos = w.p < 0 ? 0 : ((int64_t)w.p + 1) / a.ratio;
+    w.n_vis_dbg = (int32_t)min((int64_t)min(len, a.cap), by_pos);
   }
+  w.first_win_split = kMainGroups / (kWaves * gpw);
+  w.stage = a.swa_x != nullptr && (w.split + 1) * kWaves * gpw > kMainGroups;
+  w.ids_r = make_rsrc(a.topk + w.bq * 512, 2048u);
+  w.codes_r = make_rsrc(a.kv_codes + (int64_t)w.b * a.cap * 256, (uint32_t)a.cap * 256u);
+  w.scales_r = make_rsrc(a.kv_scales + (int64_t)w.b * a.cap * 32, (uint32_t)a.cap * 32u);
+  w.swa_r = make_rsrc(a.swa + (int64_t)w.b * a.S * 512, (uint32_t)a.S * 512u);
+  w.none_r = make_rsrc(a.swa, 0u);
+  return w;
+}
 
-  const int t_begin = split * a.tps;
-  const int t_end = min(kTilesPerQuery, t_begin + a.tps);
-  const int kg = tid & 7, grp = tid >> 3;  // keys 4kg..4kg+3, channels 16grp..16grp+15
-  const int32_t* tk = a.topk + bq * 512 + 4 * kg;
+// the window position of key n of window group grp
+__device__ __forceinline__ int32_t win_pos(const Wg& w, int grp) { return w.p - 127 + (grp * kKeyGroup + w.n - 512); }
 
-  // the tile's Top-K ids for this thread's four keys, as loaded (from a clamped
-  // tile): load_tile decides whether they count, since any arithmetic on them
-  // here would wait for the load
-  auto load_idx = [&](int tile) -> int4 {
-    return *reinterpret_cast<const int4*>(tk + min(tile, 512 / kAttnTile - 1) * kAttnTile);
-  };
-  // Raw bytes of a tile for this thread, left as loaded until the tile is
-  // dequantised (arithmetic on them here would wait for the loads): w[i] is the
-  // aligned 16 bytes holding a main row's 16 codes of this thread (half grp & 1)
-  // or a window row's 16 bytes, sc[i] a main row's scale byte.  Both tile kinds
-  // issue the same loads, only their addresses differ, so no branch ends with a
-  // wait: a missing entry reads row 0 (masked through vmask), and a load a tile
-  // does not need (the scale of a window row, any row of an empty cache, a tile past
-  // the split's) reads
-  // this query's Top-K row instead.
-  const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.topk + bq * 512);
-  auto load_tile = [&](int tile, int4 e4, uint4* w, uint32_t* sc, uint32_t& vmask) {
-    const bool mine = tile < t_end;                 // uniform: tiles past the split hold nothing
-    const bool main_tile = tile * kAttnTile < 512;  // uniform: 512 is a multiple of the tile
-    const bool rows = main_tile && a.cap > 0 && mine;  // uniform
-    int32_t es[4] = {mine ? e4.x : -1, mine ? e4.y : -1, mine ? e4.z : -1, mine ? e4.w : -1};
-    if (kDebug && main_tile && mine)
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (es[i] < -1 || es[i] >= n_vis_dbg) {
-          dev_flag(kErrEntryId);
-          es[i] = -1;
-        }
-    vmask = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);  // window tiles
-      vmask |= (uint32_t)(main_tile ? es[i] >= 0 : pos >= 0) << i;
-      const int64_t row = (int64_t)b * a.cap + (es[i] >= 0 ? es[i] : 0);
-      const int32_t slot = main_tile ? 0 : (pos >= 0 ? pos : 0) % a.S;
-      const uint8_t* src = rows                ? a.kv_codes + row * 256 + 16 * (grp >> 1)
-                           : main_tile || !mine ? stand_in
-                                                : a.swa + ((int64_t)b * a.S + slot) * 512 + 16 * grp;
-      w[i] = *reinterpret_cast<const uint4*>(src);
-      sc[i] = *(rows ? a.kv_scales + row * 32 + grp : stand_in);
+// the Top-K id of key n of group grp (a window group reads nothing: 0)
+__device__ __forceinline__ int32_t load_id(const Wg& w, int grp) {
+  const uint32_t off = grp < kMainGroups ? (uint32_t)(grp * kKeyGroup + w.n) * 4u : kOff;
+  return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(w.ids_r, off, 0, 0);
+}
+
+// whether key n of group grp exists: a listed id (debug builds: flagged and
+// dropped when past the visible entries), or a window position >= 0
+__device__ __forceinline__ bool key_valid(const Wg& w, int grp, int32_t& id) {
+  if (grp < kMainGroups) {
+    if (kDebug && (id < -1 || (id >= 0 && id >= w.n_vis_dbg))) {
+      dev_flag(kErrEntryId);
+      id = -1;
     }
-  };
-
-  uint4 wc[4] = {}, wn[4] = {};
-  uint32_t sc_c[4] = {}, sc_n[4] = {};
-  uint32_t vc = 0, vn = 0;
-  int4 ec = load_idx(t_begin);
-  int4 en = load_idx(t_begin + 1);
-  // the whole Top-K row, for the later tiles' ids (kept in LDS, so that the
-  // tile loop reads no ids from global memory)
-  const int2 idv = *reinterpret_cast<const int2*>(a.topk + bq * 512 + 2 * tid);
-
-  // ---------------- new window tokens (fused append): the workgroups whose
-  // tiles reach the window load all of the sequence's new tokens (at most
-  // kFusedAppendMax), two channels per thread; they are encoded into s_new
-  // once the query is in, and these workgroups also write them to the ring
-  const int first_win = 512 / (a.tps * kAttnTile);  // first split holding window tiles
-  const bool has_win = t_end * kAttnTile > 512;
-  const bool stage = a.swa_x != nullptr && has_win;
-  float2 xv[kFusedAppendMax];
-  {
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc(a.swa_x + (stage ? (int64_t)b * a.swa_T * 512 : 0), stage ? (uint32_t)a.swa_T * 2048u : 0u);
-#pragma unroll
-    for (int j = 0; j < kFusedAppendMax; j++)
-      xv[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(xr, (uint32_t)(j * 2048 + 8 * tid), 0, 0));
+    return id >= 0;
   }
+  return win_pos(w, grp) >= 0;
+}
 
-  // ---------------- query: lane holds head lane%16, dims 128*wave + 32*kk + 8*(lane/16) .. +7
-  v8h qa[4];
-  {
-    const uint16_t* qrow = a.q + (bq * 16 + (lane & 15)) * 512 + 128 * wave + 8 * (lane >> 4);
-    uint4 qraw[4];
+// issue the loads of group grp (wave-uniform kind; no branch around a load)
+__device__ __forceinline__ void issue(const Wg& w, const AttnArgs& a, int grp, int32_t id, Raw& r) {
+  const bool is_main = grp < kMainGroups;
+  const bool ok = key_valid(w, grp, id);
+  const int32_t pos = win_pos(w, grp);
+  const uint32_t slot = (uint32_t)((pos >= 0 ? pos : 0) % a.S);
+  const BufRsrc rr = is_main ? w.codes_r : w.swa_r;
+  const BufRsrc sr = is_main ? w.scales_r : w.none_r;
+  const uint32_t base = !ok ? kOff : is_main ? (uint32_t)id * 256u + 64u * w.g : slot * 512u + 128u * w.g;
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) qraw[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-    // the first two tiles' rows load while the query is scaled
-    load_tile(t_begin, ec, wc, sc_c, vc);
-    load_tile(t_begin + 1, en, wn, sc_n, vn);  // past t_end: harmless loads, never used
-    float qf[4][8];
-    float amax = 0.0f;
+  for (int j = 0; j < 8; j++) r.w[j] = buf16(rr, (is_main && j >= 4) ? kOff : base + 16u * j);
+  r.sc = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, ok ? (uint32_t)id * 32u + 8u * w.g : kOff, 0, 0));
+}
+
+// query: thread t holds head t/16, channels 32(t%16) .. +31 (bf16)
+__device__ __forceinline__ void load_query(const Wg& w, const AttnArgs& a, uint4 (&qraw)[4]) {
+  const uint16_t* qrow = a.q + (w.bq * 16 + (w.tid >> 4)) * 512 + 32 * (w.tid & 15);
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      const uint32_t xw[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
+  for (int k = 0; k < 4; k++) qraw[k] = *reinterpret_cast<const uint4*>(qrow + 8 * k);
+}
+
+// the new window tokens (fp32), channels 2t, 2t+1 of each, when this workgroup stages them
+__device__ __forceinline__ void load_new(const Wg& w, const AttnArgs& a, float2 (&xv)[kFusedAppendMax]) {
+  const BufRsrc xr = make_rsrc(a.swa_x + (w.stage ? (int64_t)w.b * a.swa_T * 512 : 0),
+                               w.stage ? (uint32_t)a.swa_T * 2048u : 0u);
 #pragma unroll
-      for (int n = 0; n < 4; n++) {
-        qf[kk][2 * n] = __uint_as_float(xw[n] << 16);
-        qf[kk][2 * n + 1] = __uint_as_float(xw[n] & 0xFFFF0000u);
-        amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * n]), fabsf(qf[kk][2 * n + 1])));
-      }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (lane < 16) s_qmax[wave][lane] = amax;
-    *reinterpret_cast<int2*>(s_ids + 2 * tid) = idv;
-    if (stage) {
-      // new token j: into s_new, and into the ring by the (query, window split)
-      // of rank j mod (Q * window splits)
-      const int n_w = Q * (a.splits - first_win), rank = qi * (a.splits - first_win) + (split - first_win);
+  for (int j = 0; j < kFusedAppendMax; j++)
+    xv[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(xr, (uint32_t)(j * 2048 + 8 * w.tid), 0, 0));
+}
+
+// The query scaled per head into fp16 (s_q [head][kQStride]) with the factor
+// that undoes the scale and applies sm_scale (s_qfac); the new window tokens
+// encoded into s_new and, by the (query, window split) of rank j mod
+// (Q * window splits), into the ring.
+__device__ __forceinline__ void stage_inputs(const Wg& w, const AttnArgs& a, const uint4 (&qraw)[4],
+                                             const float2 (&xv)[kFusedAppendMax], _Float16* s_q, float* s_qfac,
+                                             uint8_t* s_new) {
+  const int qh = w.tid >> 4, qc = 32 * (w.tid & 15);
+  float qf[32];
+  float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kFusedAppendMax; j++) {
-        if (j < a.swa_T) {
-          const uint16_t c = (uint16_t)(e4m3_encode(xv[j].x) | (e4m3_encode(xv[j].y) << 8));
-          reinterpret_cast<uint16_t*>(s_new + j * 512)[tid] = c;
-          if (j % n_w == rank && new_lo + j >= 0)  // a window shorter than the append has no slot for it
-            reinterpret_cast<uint16_t*>(a.swa + ((int64_t)b * a.S + (new_lo + j) % a.S) * 512)[tid] = c;
-        }
-      }
-    }
-    lds_barrier();
-    const int h = lane & 15;
-    const float hmax = fmaxf(fmaxf(s_qmax[0][h], s_qmax[1][h]), fmaxf(s_qmax[2][h], s_qmax[3][h]));
-    int ex;
-    frexpf(hmax, &ex);  // hmax = f * 2^ex, f in [0.5, 1); ex = 0 for a zero head
-    const int sh = min(127, max(-126, 15 - ex));
-    const float up = ldexpf(1.0f, sh);
-    if (tid < 16) s_qfac[tid] = ldexpf(a.sm_scale, -sh);
+  for (int k = 0; k < 4; k++) {
+    const uint32_t xw[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-#pragma unroll
-      for (int n = 0; n < 8; n++) qa[kk][n] = (_Float16)(qf[kk][n] * up);
+    for (int m = 0; m < 4; m++) {
+      qf[8 * k + 2 * m] = __uint_as_float(xw[m] << 16);
+      qf[8 * k + 2 * m + 1] = __uint_as_float(xw[m] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(qf[8 * k + 2 * m]), fabsf(qf[8 * k + 2 * m + 1])));
     }
   }
-  v4f acc[8];
+  amax = wave_row_reduce(amax, [](float x, float y) { return fmaxf(x, y); });  // the 16 threads of head qh
+  int ex;
+  frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1); ex = 0 for a zero head
+  const int sh = min(127, max(-126, 15 - ex));
+  const float up = ldexpf(1.0f, sh);
+  if ((w.tid & 15) == 0) s_qfac[qh] = ldexpf(a.sm_scale, -sh);
 #pragma unroll
-  for (int ct = 0; ct < 8; ct++) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-  // online softmax state: thread tid serves head tid/16 (its 16 threads are one
-  // DPP row and all hold the head's running max and sum)
-  const int sm_h = tid >> 4;
-  float m_run = -INFINITY, l_run = 0.0f;
-  lds_barrier();  // s_qfac is written
-  const float qfac = s_qfac[sm_h];
-
-  // One tile: dequantise the rows held in (w, sc, vm) into LDS, refill those
-  // registers with the tile two ahead (kRefill: so a tile's rows are in flight
-  // while the two before it are processed; past the split they read a
-  // stand-in), then S, the online softmax and O += PV.  Tiles alternate between
-  // two register sets, and no load is under a branch.  Splits of at most two
-  // tiles load both at entry and need no refill.
-  auto tile_step = [&](int tile, uint4(&w)[4], uint32_t(&sc)[4], uint32_t& vm) {
-    // ---------------- dequantise this tile's keys into LDS (fp16 [key][dim])
-    {
-      uint32_t hv[4][8];  // key i: channel pairs (2m, 2m+1) of the group, as fp16x2
-      if (tile * kAttnTile < 512) {
+  for (int k = 0; k < 4; k++) {
+    v8h h;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const uint32_t sb = ((vm >> i) & 1u) ? (sc[i] & 0xFFu) : 0u;
-          const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb * 0x0101u, 1.0f, false);
-          // this thread's half of the 16 bytes, by mask (a select here is
-          // compiled as an index into the row, which moves the rows to scratch)
-          const uint32_t odd = 0u - (uint32_t)(grp & 1);
-          fp4_group((w[i].x & ~odd) | (w[i].z & odd), s2, hv[i]);
-          fp4_group((w[i].y & ~odd) | (w[i].w & odd), s2, hv[i] + 4);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const bool valid = (vm >> i) & 1u;
-          const int32_t pos = p - 127 + (tile * kAttnTile + 4 * kg + i - 512);
-          uint4 raw = w[i];
-          if (pos >= new_lo && pos < new_hi) raw = *reinterpret_cast<const uint4*>(s_new + (pos - new_lo) * 512 + 16 * grp);
-          const uint32_t xw[4] = {valid ? raw.x : 0u, valid ? raw.y : 0u, valid ? raw.z : 0u, valid ? raw.w : 0u};
-#pragma unroll
-          for (int k = 0; k < 4; k++) {
-            hv[i][2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
-            hv[i][2 * k + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, true));
-          }
-        }
-      }
-      // [key][dim]: key 4kg+i, channels 16grp .. +15
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        uint4* dst = reinterpret_cast<uint4*>(s_k + (4 * kg + i) * kKStride + 16 * grp);
-        dst[0] = make_uint4(hv[i][0], hv[i][1], hv[i][2], hv[i][3]);
-        dst[1] = make_uint4(hv[i][4], hv[i][5], hv[i][6], hv[i][7]);
-      }
-    }
-    if (grp == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) s_valid[4 * kg + i] = (vm >> i) & 1u;
-    }
-    if constexpr (kRefill) {
-      const int4 e = *reinterpret_cast<const int4*>(s_ids + min(tile + 2, 512 / kAttnTile - 1) * kAttnTile + 4 * kg);
-      load_tile(tile + 2, e, w, sc, vm);
-    }
-    lds_barrier();
-
-    // ---------------- partial S over this wave's 128 dims
-#pragma unroll
-    for (int th = 0; th < 2; th++) {
-      v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* krow = s_k + (16 * th + (lane & 15)) * kKStride + 128 * wave + 8 * (lane >> 4);
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++) {
-        const uint4 x = *reinterpret_cast<const uint4*>(krow + 32 * kk);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kk], __builtin_bit_cast(v8h, x), sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++) s_red[wave][th][i][lane] = sacc[i];
-    }
-    lds_barrier();
-    // ---------------- scores (the four waves' partial sums) and online softmax:
-    // thread (head h, keys 2j, 2j+1); partial element (th, i, lane) is head
-    // 4*(lane/16)+i, key 16*th + lane%16
-    {
-      const int h = sm_h, k0 = 2 * (tid & 15);
-      const int th = k0 >> 4, l = 16 * (h >> 2) + (k0 & 15), i = h & 3;
-      const float s0 = s_red[0][th][i][l] + s_red[1][th][i][l] + s_red[2][th][i][l] + s_red[3][th][i][l];
-      const float s1 = s_red[0][th][i][l + 1] + s_red[1][th][i][l + 1] + s_red[2][th][i][l + 1] + s_red[3][th][i][l + 1];
-      // the head's factor undoes its query scale exactly and applies sm_scale
-      const float a0 = s_valid[k0] ? s0 * qfac : -INFINITY;
-      const float a1 = s_valid[k0 + 1] ? s1 * qfac : -INFINITY;
-      const float mt = wave_row_reduce(fmaxf(a0, a1), [](float x, float y) { return fmaxf(x, y); });
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
-      const float p0 = (a0 == -INFINITY) ? 0.0f : __expf(a0 - m_new);
-      const float p1 = (a1 == -INFINITY) ? 0.0f : __expf(a1 - m_new);
-      const float ps = wave_row_reduce(p0 + p1, [](float x, float y) { return x + y; });
-      s_p[h * kPStride + k0] = (_Float16)p0;
-      s_p[h * kPStride + k0 + 1] = (_Float16)p1;
-      m_run = m_new;
-      l_run = alpha * l_run + ps;
-      if ((tid & 15) == 0) s_alpha[h] = alpha;
-    }
-    lds_barrier();
-    // ---------------- O = alpha * O + P V
-    {
-      const uint4 pa = *reinterpret_cast<const uint4*>(s_p + (lane & 15) * kPStride + 8 * (lane >> 4));
-      const v8h pv = __builtin_bit_cast(v8h, pa);
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) al[i] = s_alpha[4 * (lane >> 4) + i];
-      // V operand of lane (group G = lane/16, column i = lane%16): keys 8G..8G+7 of
-      // dim 128*wave + 16*ct + i; lane 4j+q of the group names row 8G+j (then
-      // 8G+4+j), dims 4q..4q+3 of the block
-      const _Float16* vsrc =
-          s_k + (8 * (lane >> 4) + ((lane & 15) >> 2)) * kKStride + 128 * wave + 4 * (lane & 3);
-#pragma unroll
-      for (int ct = 0; ct < 8; ct++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) acc[ct][i] *= al[i];
-        const v4h lo = lds_read_tr16(vsrc + 16 * ct);
-        const v4h hi = lds_read_tr16(vsrc + 4 * kKStride + 16 * ct);
-        const v8h vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, vb, acc[ct], 0, 0, 0);
-      }
-    }
-    lds_barrier();
-  };
-  int tile = t_begin;
-  for (; tile + 1 < t_end; tile += 2) {
-    tile_step(tile, wc, sc_c, vc);
-    tile_step(tile + 1, wn, sc_n, vn);
+    for (int m = 0; m < 8; m++) h[m] = (_Float16)(qf[8 * k + m] * up);
+    *reinterpret_cast<v8h*>(s_q + qh * kQStride + qc + 8 * k) = h;
   }
-  if (tile < t_end) tile_step(tile, wc, sc_c, vc);
-
-  // ---------------- epilogue: rows 4*(lane/16)+i are heads, column lane%16 a dim
-  if ((tid & 15) == 0) {
-    s_m[sm_h] = m_run;
-    s_l[sm_h] = l_run;
-  }
-  lds_barrier();
-  if (a.splits == 1) {
+  if (w.stage) {
+    const int n_ws = a.splits - w.first_win_split;
+    const int n_w = a.Q * n_ws, rank = w.qi * n_ws + (w.split - w.first_win_split);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = 4 * (lane >> 4) + i;
-      const float l = s_l[h];
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-#pragma unroll
-      for (int ct = 0; ct < 8; ct++) {
-        const int dim = 128 * wave + 16 * ct + (lane & 15);
-        a.out[(bq * 16 + h) * 512 + dim] = f32_to_bf16_rne(acc[ct][i] * inv);
+    for (int j = 0; j < kFusedAppendMax; j++) {
+      if (j < a.swa_T) {
+        const uint16_t c = (uint16_t)(e4m3_encode(xv[j].x) | (e4m3_encode(xv[j].y) << 8));
+        reinterpret_cast<uint16_t*>(s_new + j * 512)[w.tid] = c;
+        if (j % n_w == rank && w.new_lo + j >= 0)  // a window shorter than the append has no slot for it
+          reinterpret_cast<uint16_t*>(a.swa + ((int64_t)w.b * a.S + (w.new_lo + j) % a.S) * 512)[w.tid] = c;
       }
-    }
-    if (a.lse && tid < 16) a.lse[bq * 16 + tid] = s_l[tid] > 0.0f ? s_m[tid] + __logf(s_l[tid]) : -INFINITY;
-    return;
-  }
-  {
-    // the split's output normalised by its own sum: |value| <= the largest key
-    // value (2688), so fp16 holds it to 2^-12 relative
-    _Float16* po = a.part_o + ((int64_t)split * a.bq_total + bq) * 16 * 512;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = 4 * (lane >> 4) + i;
-      const float l = s_l[h];
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-#pragma unroll
-      for (int ct = 0; ct < 8; ct++) po[h * 512 + 128 * wave + 16 * ct + (lane & 15)] = (_Float16)(acc[ct][i] * inv);
-    }
-    if (tid < 16) {
-      float* pm = a.part_ml + ((int64_t)split * a.bq_total + bq) * 32;
-      pm[2 * tid] = s_m[tid];
-      pm[2 * tid + 1] = s_l[tid];
     }
   }
 }
 
-// One workgroup per (query, head): combine the splits' normalised partials,
-// each weighted by its sum times exp(its max - the overall max); each thread
-// owns two of the 512 output channels.
-__global__ void __launch_bounds__(kThreads)
-    attend_merge_kernel(const _Float16* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
+// This lane's quarter of key n of group grp as fp16 pairs: kh[c] holds
+// channels 128g + 2c, 2c + 1.  A window token appended by this call comes from s_new.
+__device__ __forceinline__ void dequant(const Wg& w, int grp, const Raw& r, const uint8_t* s_new, uint32_t (&kh)[64]) {
+  if (grp < kMainGroups) {
+    const uint32_t scw[2] = {r.sc.x, r.sc.y};
+#pragma unroll
+    for (int sg = 0; sg < 8; sg++) {  // scale group sg: channels 128g + 16sg .. +15
+      const uint32_t sb = (scw[sg >> 2] >> (8 * (sg & 3))) & 0xFFu;
+      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb * 0x0101u, 1.0f, false);
+      const uint4 w4 = r.w[sg >> 1];
+      const uint32_t c0 = (sg & 1) ? w4.z : w4.x, c1 = (sg & 1) ? w4.w : w4.y;
+      fp4_word(c0, s2, kh + 8 * sg);
+      fp4_word(c1, s2, kh + 8 * sg + 4);
+    }
+  } else {
+    const int32_t pos = win_pos(w, grp);
+    const bool fresh = pos >= w.new_lo && pos < w.new_hi;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      uint4 x = r.w[j];
+      if (fresh) x = *reinterpret_cast<const uint4*>(s_new + (pos - w.new_lo) * 512 + 128 * w.g + 16 * j);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        kh[8 * j + 2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
+        kh[8 * j + 2 * k + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, true));
+      }
+    }
+  }
+}
+
+// S^T = K Q^T for one group: st[i] = head n's (scaled) score of key 4g + i.
+// Step kb pairs channels 128g' + 8kb .. +7 of every quarter g' on both operands.
+__device__ __forceinline__ v4f score_group(const uint32_t (&kh)[64], const _Float16* s_q, int n, int g) {
+  v4f st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 16; kb++) {
+    const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
+    const v8h qb = *reinterpret_cast<const v8h*>(s_q + n * kQStride + 128 * g + 8 * kb);
+    st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, st, 0, 0, 0);
+  }
+  return st;
+}
+
+// the group's keys into a V tile [key][channel]: row n, channels 128g ..
+__device__ __forceinline__ void store_tile(const uint32_t (&kh)[64], _Float16* rows, int n, int g) {
+#pragma unroll
+  for (int c = 0; c < 16; c++)
+    *reinterpret_cast<uint4*>(rows + n * kVStride + 128 * g + 8 * c) =
+        make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
+}
+
+// Decode: one group of 16 keys per wave, 64 keys per workgroup, ten workgroups
+// (splits) per query.  The waves share their scores through LDS (16 heads x 64
+// keys), each takes the softmax over all 64, and wave w then owns output
+// channels 128w .. 128w+127 of P V over the workgroup's four dequantised key
+// groups, so the waves never combine output vectors.  Writes the unnormalised
+// fp32 partial and the (max, sum) per head.
+constexpr int kSStride = 68;  // fp32 per head row of the shared scores (64 keys + pad)
+__global__ void __launch_bounds__(kThreads) attend_decode_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[16 * kQStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // the 64 keys [key][channel]
+  __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
+  __shared__ float s_qfac[16];
+  const Wg w = make_wg(a, 1);
+  const int n = w.n, g = w.g, wave = w.wave;
+  const int grp = w.split * kWaves + wave;
+
+  int32_t id = load_id(w, grp);
+  uint4 qraw[4];
+  load_query(w, a, qraw);
+  float2 xv[kFusedAppendMax];
+  load_new(w, a, xv);
+  Raw r;
+  issue(w, a, grp, id, r);
+  stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
+  lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
+  const float qfac = s_qfac[n];
+  const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id)) & 0xFFFFu;  // bit k: key k exists
+
+  uint32_t kh[64];
+  dequant(w, grp, r, s_new, kh);
+  const v4f st = score_group(kh, s_q, n, g);
+  store_tile(kh, s_v + wave * 16 * kVStride, n, g);
+  {
+    v4f sc;
+#pragma unroll
+    for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
+    *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
+  }
+  lds_barrier();  // every wave's scores and keys are in
+
+  // ---------------- softmax of head n over the 64 keys: this lane holds keys 32kb + 8g .. +7
+  float sv[2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) {
+    const v4f lo = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g);
+    const v4f hi = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sv[kb][i] = lo[i];
+      sv[kb][4 + i] = hi[i];
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[kb][i]);
+  mx = rows_max(mx);
+  float ps = 0.0f;
+  v8h pb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - mx);
+      ps += pv;
+      pb[kb][i] = (_Float16)pv;
+    }
+  ps = rows_sum(ps);
+
+  // ---------------- O^T = V^T P^T for channels 128 wave .. +127: tile ct, key block kb
+  v4f acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; c++) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) {
+    const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const v4h lo = lds_read_tr16(vsrc + 16 * c);
+      const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
+      const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
+    }
+  }
+  // acc[c][i] = O[head n][channel 128 wave + 16c + 4g + i], relative to mx
+  float* po = a.part_o + ((int64_t)w.split * a.bq_total + w.bq) * 16 * 512 + n * 512 + 128 * wave + 4 * g;
+#pragma unroll
+  for (int c = 0; c < 8; c++) *reinterpret_cast<v4f*>(po + 16 * c) = acc[c];
+  if (wave == 0 && g == 0) {
+    float* pm = a.part_ml + ((int64_t)w.split * a.bq_total + w.bq) * 32;
+    pm[2 * n] = mx;
+    pm[2 * n + 1] = ps;
+  }
+}
+
+// Several groups per wave (more queries, fewer splits): every wave runs its
+// groups start to finish with an online softmax, the next group's rows in
+// flight while one is processed, and the four waves' (max, sum, O) are
+// combined through LDS at the end.  One split writes the bf16 output, several
+// their fp32 partials.
+template <int kGpw>  // groups per wave
+__global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[16 * kQStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // V tiles, then the exchange
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+  __shared__ float s_qfac[16];
+
+  const Wg w = make_wg(a, kGpw);
+  const int n = w.n, g = w.g, wave = w.wave, tid = w.tid;
+  const int64_t bq = w.bq;
+  const int split = w.split;
+  // this wave's groups: grp0 .. grp0 + kGpw - 1
+  const int grp0 = (split * kWaves + wave) * kGpw;
+
+  // ---------------- ids first, then the query and the new window tokens, then the first rows
+  int32_t ids[kGpw + 2];  // two spare slots: the prefetch indices below stay in bounds
+  ids[0] = load_id(w, grp0);
+  if constexpr (kGpw > 1) ids[1] = load_id(w, grp0 + 1);
+  uint4 qraw[4];
+  load_query(w, a, qraw);
+  float2 xv[kFusedAppendMax];
+  load_new(w, a, xv);
+  Raw raw[2];
+  issue(w, a, grp0, ids[0], raw[0]);
+  stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
+  lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
+  const float qfac = s_qfac[n];
+
+  v4f acc[32];  // O^T: acc[ct][i] = O[head n][channel 16ct + 4g + i]
+#pragma unroll
+  for (int ct = 0; ct < 32; ct++) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  _Float16* vt = s_v + wave * 16 * kVStride;
+
+#pragma unroll
+  for (int gi = 0; gi < kGpw; gi++) {
+    const int grp = grp0 + gi;
+    Raw& r = raw[gi & 1];
+    // the next group's rows (its id loaded a group ago), and the id after it
+    if (gi + 1 < kGpw) {
+      if (gi + 2 < kGpw) ids[gi + 2] = load_id(w, grp0 + gi + 2);
+      issue(w, a, grp + 1, ids[gi + 1], raw[(gi + 1) & 1]);
+    }
+    int32_t id_c = ids[gi];
+    const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id_c)) & 0xFFFFu;  // bit k: key k exists
+
+    uint32_t kh[64];
+    dequant(w, grp, r, s_new, kh);
+    const v4f st = score_group(kh, s_q, n, g);
+    store_tile(kh, vt, n, g);
+
+    // ---------------- online softmax: st[i] is head n, key 4g + i
+    float s[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      s[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
+    v4h pk;
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float pv = (s[i] == -INFINITY) ? 0.0f : __expf(s[i] - m_new);
+      ps += pv;
+      pk[i] = (_Float16)pv;
+    }
+    ps = rows_sum(ps);
+    m_run = m_new;
+    l_run = alpha * l_run + ps;
+    lds_wave_sync();  // the V tile is written
+
+    // ---------------- O^T = alpha O^T + V^T P^T, one 16-channel tile ct at a time
+    const _Float16* vsrc = vt + (4 * g + (n >> 2)) * kVStride + 4 * (n & 3);
+#pragma unroll
+    for (int ct = 0; ct < 32; ct++) {
+      const v4h va = lds_read_tr16(vsrc + 16 * ct);
+      if (gi > 0) {  // nothing accumulated before the first group
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[ct][i] *= alpha;
+      }
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pk, acc[ct], 0, 0, 0);
+    }
+    lds_wave_sync();  // the tile is read before the next group overwrites it
+  }
+
+  // ---------------- combine the four waves: max and sum per head, then O
+  if (g == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_run;
+  }
+  lds_barrier();  // every wave is past its key loop: the V tiles are free
+  // this wave's weight for head n: exp(its max - the workgroup's max)
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; w++) M = fmaxf(M, s_m[w][n]);
+  const float own = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
+  float* sx = reinterpret_cast<float*>(s_v);  // [wave][head][kXStride]
+  const int oh = tid >> 4, oc = 16 * (tid & 15);  // combine: head oh, channels oc .. oc+15 of the half
+  // the workgroup's max and sum for head oh
+  float Lh = 0.0f, Mh = -INFINITY;
+  {
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) Mh = fmaxf(Mh, s_m[w][oh]);
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+      const float mw = s_m[w][oh];
+      Lh += (mw == -INFINITY ? 0.0f : __expf(mw - Mh)) * s_l[w][oh];
+    }
+  }
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+#pragma unroll
+    for (int c = 0; c < 16; c++) {
+      const int ct = 16 * half + c;
+      const v4f v = acc[ct] * own;
+      *reinterpret_cast<v4f*>(sx + (wave * 16 + n) * kXStride + 16 * c + 4 * g) = v;
+    }
+    lds_barrier();
+    float o[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) o[k] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; k4++) {
+        const v4f v = *reinterpret_cast<const v4f*>(sx + (w * 16 + oh) * kXStride + oc + 4 * k4);
+#pragma unroll
+        for (int i = 0; i < 4; i++) o[4 * k4 + i] += v[i];
+      }
+    }
+    const int ch = 256 * half + oc;  // first output channel of this thread
+    if (a.splits == 1) {
+      const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
+      uint32_t pk2[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        pk2[k] = (uint32_t)f32_to_bf16_rne(o[2 * k] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * k + 1] * inv) << 16);
+      uint4* dst = reinterpret_cast<uint4*>(a.out + (bq * 16 + oh) * 512 + ch);
+      dst[0] = make_uint4(pk2[0], pk2[1], pk2[2], pk2[3]);
+      dst[1] = make_uint4(pk2[4], pk2[5], pk2[6], pk2[7]);
+    } else {
+      float4* dst = reinterpret_cast<float4*>(a.part_o + (((int64_t)split * a.bq_total + bq) * 16 + oh) * 512 + ch);
+#pragma unroll
+      for (int k4 = 0; k4 < 4; k4++) dst[k4] = make_float4(o[4 * k4], o[4 * k4 + 1], o[4 * k4 + 2], o[4 * k4 + 3]);
+    }
+    if (half == 0) lds_barrier();  // the exchange is read before the second half overwrites it
+  }
+  if ((tid & 15) == 0) {
+    if (a.splits == 1) {
+      if (a.lse) a.lse[bq * 16 + oh] = Lh > 0.0f ? Mh + __logf(Lh) : -INFINITY;
+    } else {
+      float* pm = a.part_ml + ((int64_t)split * a.bq_total + bq) * 32;
+      pm[2 * oh] = Mh;
+      pm[2 * oh + 1] = Lh;
+    }
+  }
+}
+
+// One workgroup per (query, head): combine the splits' unnormalised partials,
+// each weighted by exp(its max - the overall max); each thread owns four of the
+// 512 output channels.
+constexpr int kMergeThreads = 128;
+__global__ void __launch_bounds__(kMergeThreads)
+    attend_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits,
                         int64_t bq_total, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kMax = 10;
   const int64_t wr = xcd_rank(blockIdx.x, bq_total * 16);  // the XCD of the query's attention splits
   const int64_t bq = wr >> 4;
   const int h = (int)(wr & 15);
   const int tid = threadIdx.x;
   // every load is issued from a clamped split so they all stay in flight together
-  float ms[kMaxSplits], ls[kMaxSplits];
-  v2h v[kMaxSplits];
+  float ms[kMax], ls[kMax];
+  float4 v[kMax];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; s++) {
+  for (int s = 0; s < kMax; s++) {
     const int sc = min(s, splits - 1);
     const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((int64_t)sc * bq_total + bq) * 32 + 2 * h);
     ms[s] = ml.x;
     ls[s] = ml.y;
-    v[s] = *reinterpret_cast<const v2h*>(part_o + (((int64_t)sc * bq_total + bq) * 16 + h) * 512 + 2 * tid);
+    v[s] = *reinterpret_cast<const float4*>(part_o + (((int64_t)sc * bq_total + bq) * 16 + h) * 512 + 4 * tid);
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; s++)
+  for (int s = 0; s < kMax; s++)
     if (s < splits) M = fmaxf(M, ms[s]);
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; s++) {
-    const float w = (s < splits && ms[s] != -INFINITY) ? __expf(ms[s] - M) * ls[s] : 0.0f;
-    L += w;
-    o0 += w * (float)v[s][0];
-    o1 += w * (float)v[s][1];
+  for (int s = 0; s < kMax; s++) {
+    const float w = (s < splits && ms[s] != -INFINITY) ? __expf(ms[s] - M) : 0.0f;
+    L += w * ls[s];
+    o0 += w * v[s].x;
+    o1 += w * v[s].y;
+    o2 += w * v[s].z;
+    o3 += w * v[s].w;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const uint32_t packed = (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16);
-  reinterpret_cast<uint32_t*>(out + (bq * 16 + h) * 512)[tid] = packed;
+  const uint2 packed = make_uint2(
+      (uint32_t)f32_to_bf16_rne(o0 * inv) | ((uint32_t)f32_to_bf16_rne(o1 * inv) << 16),
+      (uint32_t)f32_to_bf16_rne(o2 * inv) | ((uint32_t)f32_to_bf16_rne(o3 * inv) << 16));
+  reinterpret_cast<uint2*>(out + (bq * 16 + h) * 512)[tid] = packed;
   if (lse && tid == 0) lse[bq * 16 + h] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
 
@@ -537,7 +711,6 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
   a.sm_scale = sm_scale;
   a.Q = Q;
   a.splits = attend_splits(bq);
-  a.tps = tiles_per_split(a.splits);
   a.out = out;
   a.lse = lse;
   a.part_o = nullptr;
@@ -545,18 +718,20 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
   a.bq_total = bq;
   if (a.splits > 1) {
     uint8_t* base = (uint8_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-    a.part_o = (_Float16*)base;
-    a.part_ml = (float*)(a.part_o + (int64_t)a.splits * bq * 16 * 512);
+    a.part_o = (float*)base;
+    a.part_ml = a.part_o + (int64_t)a.splits * bq * 16 * 512;
   }
   const unsigned n_wg = (unsigned)(a.splits * bq);  // (split, query) pairs in XCD-aware order
-  if (a.tps > 2)
-    hipLaunchKernelGGL(attend_kernel<true>, dim3(n_wg), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attend_kernel<false>, dim3(n_wg), dim3(kThreads), 0, stream, a);
+  switch (a.splits) {
+    case 10: hipLaunchKernelGGL(attend_decode_kernel, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(attend_kernel<2>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attend_kernel<5>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(attend_kernel<10>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(bq * 16)), dim3(kThreads), 0, stream, a.part_o, a.part_ml,
-                     a.splits, bq, out, lse);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(bq * 16)), dim3(kMergeThreads), 0, stream, a.part_o,
+                     a.part_ml, a.splits, bq, out, lse);
   return hipGetLastError();
 }
 

@@ -48,7 +48,6 @@ IndexWs index_ws_carve(void* ws, int64_t bq, int32_t capacity);
 
 // ---- attention geometry
 constexpr int kAttnKeys = 640;  // 512 selected + 128 window
-constexpr int kAttnTile = 32;
 int attend_splits(int64_t bq);
 size_t attend_ws_bytes(int64_t bq);
 

@@ -67,7 +67,7 @@ def test_workspace_sizes(csa):
     a = ws(csa.OP_INDEX, 16, 1, 131072)
     assert a > 0 and ws(csa.OP_INDEX, 32, 1, 131072) > a and ws(csa.OP_INDEX, 16, 1, 262144) > a
     assert ws(csa.OP_ATTEND, 16, 1, 0) > 0
-    assert ws(csa.OP_ATTEND, 1, 512, 0) == 0  # enough queries: no split, no workspace
+    assert ws(csa.OP_ATTEND, 1, 2048, 0) == 0  # enough queries: no split, no workspace
     assert ws(csa.OP_ATTEND, 1, 300, 0) > 0  # 300 queries split in two
 
 
