@@ -73,7 +73,7 @@ def _declare(L):
     L.orc_compress_pairs.argtypes = [f32p, f32p, i64, f32p]
     L.orc_compress.argtypes = [f32p, f32p, ctypes.c_int32, i64, f32p]
     L.orc_quantize_query.argtypes = [f32p, u8p, f32p]
-    L.orc_entry_score.restype = ctypes.c_float
+    L.orc_entry_score.restype = ctypes.c_double
     L.orc_entry_score.argtypes = [u8p, f32p, f32p, u8p, ctypes.c_float]
     L.orc_quantize_append.restype = ctypes.c_int
     L.orc_quantize_append.argtypes = [u8p, u8p, u8p, f32p, i32p, i32, i32, i32, f32p, f32p, f32p, i32]
@@ -81,7 +81,7 @@ def _declare(L):
     L.orc_swa_append.argtypes = [u8p, i32, f32p, i32p, i32, i32]
     L.orc_index_topk.restype = ctypes.c_int
     L.orc_index_topk.argtypes = [u8p, f32p, i32p, i32, i32, i32, ctypes.c_int, f32p, f32p, i32p, i32p,
-                                 i32p, i32p, i32, f32p]
+                                 i32p, i32p, i32, f64p]
     L.orc_attend.restype = ctypes.c_int
     L.orc_attend.argtypes = [u8p, u8p, i32p, i32, i32, i32, i32p, u8p, i32, f32p, i32p, ctypes.c_float,
                              f64p, f64p, i32]
@@ -298,12 +298,12 @@ def index_topk(cache: Cache, mode: int, iq, iw=None, q_pos=None, pool_in=None, w
     pool_in = _c(pool_in, np.int32)
     topk = np.empty((B, Q, TOPK), np.int32)
     pool = np.empty((B, Q, POOL), np.int32) if want_pool else None
-    scores = np.empty((B, Q, cache.cap), np.float32) if want_scores else None
+    scores = np.empty((B, Q, cache.cap), np.float64) if want_scores else None
     rc = lib().orc_index_topk(_p(cache.ik_codes, ctypes.c_uint8), _p(cache.ik_scales, ctypes.c_float),
                               _p(cache.length, ctypes.c_int32), cache.B, cache.cap, cache.ratio, int(mode),
                               _p(iq, ctypes.c_float), _p(iw, ctypes.c_float), _p(q_pos, ctypes.c_int32),
                               _p(pool_in, ctypes.c_int32), _p(topk, ctypes.c_int32), _p(pool, ctypes.c_int32), Q,
-                              _p(scores, ctypes.c_float))
+                              _p(scores, ctypes.c_double))
     _check(rc, "index_topk")
     return topk, pool, scores
 

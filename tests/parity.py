@@ -5,10 +5,11 @@
   its set must equal the oracle's except for pairs swapped across the selection
   boundary whose oracle scores both lie within 1e-6 relative of the oracle's
   K-th score (the boundary score S_b; when S_b == 0 the bound is 1e-6 times the
-  best score).  The GPU accumulates the exact E4M3 products on the bf16 matrix
-  cores in fp32 (measured within about 1e-7 relative of the exact dot on the
-  largest dots), the oracle rounds the exact dot once, so swaps can only come
-  from accumulation-order differences well below that bound.
+  best score).  The oracle's scores are the definition evaluated in fp64 (exact
+  E4M3 dot products); the GPU sums the same exact products on the bf16 matrix
+  cores in fp32 (within about 1e-7 relative of the exact dot on the largest
+  dots) and takes the head sum and the key-scale product in fp32, so the two
+  scores differ by rounding only, an order of magnitude inside that bound.
 * Attention outputs: |gpu - ref| <= 2e-3 + 1e-2 * |ref| elementwise.
 """
 import numpy as np

@@ -42,8 +42,9 @@ def test_score_hand_example(orc):
     assert orc.entry_score(q8c, sqc, w, k8[0], sk[0]) == 200704.0 + 2 * 2 * 448
 
 
-def test_single_head_dot_is_exact_then_rounded_once(orc):
-    """With unit scales and one head, score == fp32(exact dot) when positive."""
+def test_single_head_dot_is_exact(orc):
+    """With unit scales and one head, the score is the exact dot when positive
+    (the 64-term dot of E4M3 values fits in 53 bits), else 0."""
     rng = np.random.default_rng(5)
     finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
     sq = np.array([1, 0, 0, 0], np.float32)
@@ -57,9 +58,47 @@ def test_single_head_dot_is_exact_then_rounded_once(orc):
         q8 = np.zeros((4, 64), np.uint8)
         q8[0] = qrow
         exact = sum(a * b for a, b in zip(_e4m3_exact(qrow), _e4m3_exact(k8)))
-        want = np.float32(float(exact)) if exact > 0 else np.float32(0.0)
+        want = float(exact) if exact > 0 else 0.0
+        assert Fraction(want) == max(exact, Fraction(0)), "the exact dot is representable"
         got = orc.entry_score(q8, sq, None, k8, 1.0)
         assert got == want, (trial, float(exact), got)
+
+
+def test_multi_head_score_against_exact_rationals(orc):
+    """Four heads with non-unit query and key scales and head weights (some
+    negative, some zero) against the definition evaluated in exact rational
+    arithmetic: s_k * sum_h w_h * s_qh * max(q8_h . k8, 0).  The oracle rounds
+    the head products, the head sum and the key-scale product at fp64 precision,
+    so it lies within a few units of 2^-53 of the sum of the terms' magnitudes
+    (the usual bound for a sum whose terms may cancel)."""
+    rng = np.random.default_rng(17)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n_pos = 0
+    for trial in range(200):
+        iq = rng.standard_normal((4, 64)).astype(np.float32) * np.float32(rng.choice([1e-3, 0.7, 3.0, 250.0]))
+        if trial % 5 == 0:
+            iq[rng.integers(0, 4)] = 0.0  # a zero head: s_q = 0
+        q8, sq = orc.quantize_query(iq)
+        k8 = rng.choice(finite, 64).astype(np.uint8)
+        sk = np.float32(rng.choice([2.0 ** -9, 0.013, 1.0, 6.5]) * rng.uniform(0.5, 2.0))
+        w = (rng.standard_normal(4) * 2).astype(np.float32)
+        if trial % 4 == 0:
+            w[rng.integers(0, 4)] = 0.0
+        kv = _e4m3_exact(k8)
+        exact, mag = Fraction(0), Fraction(0)
+        for h in range(4):
+            dot = sum(a * b for a, b in zip(_e4m3_exact(q8[h]), kv))
+            term = Fraction(float(w[h])) * Fraction(float(sq[h])) * max(dot, Fraction(0))
+            exact += term
+            mag += abs(term)
+        exact *= Fraction(float(sk))
+        mag *= Fraction(float(sk))
+        got = orc.entry_score(q8, sq, w, k8, float(sk))
+        n_pos += exact > 0
+        assert abs(Fraction(got) - exact) <= mag * Fraction(8, 2 ** 53), (trial, float(exact), got)
+        if mag == abs(exact):  # no cancellation (non-negative weights): relative error bound
+            assert abs(Fraction(got) - exact) <= abs(exact) * Fraction(4, 2 ** 53)
+    assert n_pos > 20  # the cases are not all clipped to zero
 
 
 def _cache_with_ik(orc, B, E, cap, seed_tag, cid=90, scale_rows=None):
