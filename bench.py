@@ -226,8 +226,13 @@ class OracleStep:
                         q=[pick(t[:hs].float().cpu().numpy()) for t in inp["q"]])
         self.q_pos = pick(wl.q_pos[:hs].cpu().numpy()) if wl.q_pos is not None else None
 
-    def step(self, want_scores=False):
-        """One group step; returns per-layer dict(topk, pool, scores, out)."""
+    def step(self, want_scores=False, gpu_used=None):
+        """One group step; returns per-layer dict(topk, pool, scores, out, out_cmp).
+
+        gpu_used[l], if given, is the Top-K list [hs][Q'][512] the GPU's layer l
+        attended with; out_cmp is the oracle's attention over that list (its own
+        `out` when the two lists agree), so that a boundary swap still leaves
+        every attention output comparable."""
         orc, wl, oc, inp = self.orc, self.wl, self.oc, self.inp
         if not wl.decode:
             oc.length[:] = wl.E_before
@@ -245,7 +250,11 @@ class OracleStep:
                 topk, _, scores = orc.index_topk(oc, orc.REINDEX, inp["iq"][l], q_pos=self.q_pos, pool_in=pool,
                                                  want_scores=want_scores)
             out, lse = orc.attend(oc, topk, self.swas[l], inp["q"][l], SM_SCALE, q_pos=self.q_pos)
-            res.append(dict(topk=topk, pool=pool if mode == "full_pool" else None, scores=scores, out=out, lse=lse))
+            out_cmp = out
+            if gpu_used is not None and not np.array_equal(gpu_used[l], topk):
+                out_cmp, _ = orc.attend(oc, gpu_used[l], self.swas[l], inp["q"][l], SM_SCALE, q_pos=self.q_pos)
+            res.append(dict(topk=topk, pool=pool if mode == "full_pool" else None, scores=scores, out=out, lse=lse,
+                            out_cmp=out_cmp))
         return res
 
 
@@ -455,8 +464,10 @@ class OracleSchedule38:
                         q=[[h(x) for x in xs] for xs in inp["q"]])
         self.q_pos = [np.full((hs, 1), wl.ctx + t, np.int32) for t in range(2)]
 
-    def step(self, want_scores=False):
-        """Returns res[t][l] = dict(topk, pool, scores, out) for token t and layer l."""
+    def step(self, want_scores=False, gpu_used=None):
+        """Returns res[t][l] = dict(topk, pool, scores, out, out_cmp) for token t and
+        layer l; gpu_used[t][l] as in OracleStep.step (the ring and caches are as
+        they were at that layer when out_cmp is computed)."""
         orc, wl, oc, inp = self.orc, self.wl, self.oc, self.inp
         for n, c in oc.items():
             c.length[:] = wl.E0[n]
@@ -482,7 +493,11 @@ class OracleSchedule38:
                     topk, _, scores = orc.index_topk(c, orc.REINDEX, inp["iq"][t][l], q_pos=self.q_pos[t],
                                                      pool_in=pool, want_scores=want_scores)
                 out, _ = orc.attend(c, topk, self.swas[l], inp["q"][t][l], SM_SCALE, q_pos=self.q_pos[t])
-                res[t][l] = dict(topk=topk, pool=lpool, scores=scores, out=out)
+                out_cmp = out
+                if gpu_used is not None and not np.array_equal(gpu_used[t][l], topk):
+                    out_cmp, _ = orc.attend(c, gpu_used[t][l], self.swas[l], inp["q"][t][l], SM_SCALE,
+                                            q_pos=self.q_pos[t])
+                res[t][l] = dict(topk=topk, pool=lpool, scores=scores, out=out, out_cmp=out_cmp)
         return res
 
 

@@ -55,7 +55,7 @@ class CacheStruct(ctypes.Structure):
                 ("capacity", ctypes.c_int32), ("ratio", ctypes.c_int32)]
 
 
-EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_swa_append", "csa2_index_score_topk",
+EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_compress", "csa2_swa_append", "csa2_index_score_topk",
            "csa2_sparse_attend", "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
 
 
@@ -69,6 +69,8 @@ def _load(path):
     L.csa2_quantize_append.argtypes = [cp, vp, vp, vp, i32, i32, vp]
     L.csa2_quantize_append_proj.restype = ctypes.c_int
     L.csa2_quantize_append_proj.argtypes = [cp, vp, vp, vp, i32, i32, vp]
+    L.csa2_compress.restype = ctypes.c_int
+    L.csa2_compress.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     L.csa2_swa_append.restype = ctypes.c_int
     L.csa2_swa_append.argtypes = [vp, i32, vp, vp, i32, i32, vp]
     L.csa2_index_score_topk.restype = ctypes.c_int
@@ -201,6 +203,20 @@ def quantize_append_proj(cache: Cache, kv, w_ik, logits=None, stream=None):
                                          cache.host_len_bound, _stream(stream))
     _check(rc, "csa2_quantize_append_proj")
     cache.host_len_bound += T // cache.ratio
+
+
+def compress(kv, ratio, logits=None, out=None, stream=None):
+    """csa2_compress: [B][T][512] token latents -> [B][T/ratio][512] fp32 entries."""
+    B, T = kv.shape[0], kv.shape[1]
+    _expect(kv, torch.float32, (B, T, D), "kv")
+    if logits is not None:
+        _expect(logits, torch.float32, (B, T, D), "logits")
+    if out is None:
+        out = torch.empty((B, T // ratio, D), dtype=torch.float32, device=kv.device)
+    _expect(out, torch.float32, (B, T // ratio, D), "out")
+    rc = lib().csa2_compress(_ptr(kv), _ptr(logits), B, T, ratio, _ptr(out), _stream(stream))
+    _check(rc, "csa2_compress")
+    return out
 
 
 def swa_append(swa, x, seq_len, stream=None):

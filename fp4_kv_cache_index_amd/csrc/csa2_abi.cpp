@@ -89,6 +89,17 @@ int csa2_quantize_append_proj(const csa2_cache* cache, const float* kv, const fl
   return quantize_append_impl(cache, kv, logits, nullptr, w_ik, T, host_len_bound, stream);
 }
 
+int csa2_compress(const float* kv, const float* logits, int32_t B, int32_t T, int32_t ratio, float* out,
+                  void* stream) {
+  if (B < 0 || T < 0 || ratio < 1 || ratio > kMaxRatio || T % ratio != 0) return CSA2_EINVAL;
+  if ((ratio >= 2) != (logits != nullptr)) return CSA2_EINVAL;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (!kv || !out || !aligned(kv, 4) || !aligned(out, 4) || (logits && !aligned(logits, 4))) return CSA2_EINVAL;
+  const int rc = device_status(stream);
+  if (rc != CSA2_OK) return rc;
+  return from_hip(csa2::launch_compress(kv, logits, B, T, ratio, out, (hipStream_t)stream));
+}
+
 int csa2_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,
                     void* stream) {
   if (S < 1 || B < 0 || T < 0 || T > S) return CSA2_EINVAL;

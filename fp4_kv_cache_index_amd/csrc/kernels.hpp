@@ -68,6 +68,8 @@ hipError_t launch_quant_append(const LaunchCache& c, const float* kv, const floa
                                const float* w_ik, int32_t T, hipStream_t stream);
 hipError_t launch_swa_append(uint8_t* swa, int32_t S, const float* x, const int32_t* seq_len, int32_t B, int32_t T,
                              hipStream_t stream);
+hipError_t launch_compress(const float* kv, const float* logits, int32_t B, int32_t T, int32_t ratio, float* out,
+                           hipStream_t stream);
 hipError_t launch_index(const LaunchCache& c, int mode, const float* iq, const float* iw, const int32_t* q_pos,
                         const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws,
                         hipStream_t stream);

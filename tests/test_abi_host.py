@@ -129,6 +129,19 @@ def test_swa_rejections(csa, L):
     assert s(p, 128, p, p, 0, 1, None) == csa.OK
 
 
+def test_compress_rejections(csa, L):
+    p = ctypes.c_void_p(FAKE)
+    c = L.csa2_compress
+    assert c(p, p, 1, 3, 2, p, None) == csa.EINVAL  # T % ratio
+    assert c(p, None, 1, 4, 2, p, None) == csa.EINVAL  # ratio 2 needs logits
+    assert c(p, p, 1, 4, 1, p, None) == csa.EINVAL  # ratio 1 takes none
+    assert c(p, p, 1, 34, 17, p, None) == csa.EINVAL  # ratio above 16
+    assert c(None, p, 1, 4, 2, p, None) == csa.EINVAL
+    assert c(p, p, 1, 4, 2, None, None) == csa.EINVAL
+    assert c(p, p, -1, 4, 2, p, None) == csa.EINVAL
+    assert c(p, p, 0, 4, 2, p, None) == csa.OK and c(p, p, 3, 0, 2, p, None) == csa.OK
+
+
 def test_index_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     f = L.csa2_index_score_topk

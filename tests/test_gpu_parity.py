@@ -87,6 +87,36 @@ def test_quantize_append_bitexact(csa, orc, B, T, ratio, pre):
     assert np.array_equal(host(gc.ik_scales).view(np.uint32), oc.ik_scales.view(np.uint32))
 
 
+@pytest.mark.parametrize("ratio,T", [(2, 2048), (3, 300), (4, 512), (8, 256), (16, 512)])
+def test_compress_split_check(csa, orc, ratio, T):
+    """The compression step on its own (ratio-m entries before quantisation):
+    (i) the GPU's fp32 entries equal the oracle's within 1e-6 relative (both
+    evaluate the rule in fp64 without fused multiply-adds and round once; the
+    device and host exp may differ in the last fp64 bits); (ii) quantising the
+    GPU's own fp32 entries gives the oracle's FP4 bytes bit for bit, so any
+    difference in the appended cache could only come from (i)."""
+    B = 2
+    kv = special_rows(B * T).reshape(B, T, 512)
+    lg = synth.normal(13, f"lg{ratio}", (B, T, 512)) * np.float32(3.0)
+    lg[0, :ratio] = 0.0  # equal logits: the mean of the tokens
+    got = host(csa.compress(dev(kv), ratio, logits=dev(lg)))
+    want = orc.compress(kv.reshape(B * T, 512), lg.reshape(B * T, 512), ratio).reshape(B, T // ratio, 512)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=0.0)
+    n_diff = int((got.view(np.uint32) != want.view(np.uint32)).sum())
+    print(f"ratio {ratio}: {got.size} entries, {n_diff} differ in the last bits")
+    # identical fp32 inputs quantise to identical bytes (a ratio-1 append of the GPU's entries)
+    n = T // ratio
+    gc = csa.Cache(B, n + 1, 1)
+    ik = synth.normal(13, "ik", (B, n, 64))
+    csa.quantize_append(gc, dev(got), dev(ik))
+    oc = orc.Cache(B, n + 1, 1)
+    orc.quantize_append(oc, got, ik)
+    assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
+    assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
+    # ratio 1 is a copy
+    assert np.array_equal(host(csa.compress(dev(kv), 1)), kv)
+
+
 @pytest.mark.parametrize("B,T,ratio", [
     (3, 1, 1),       # decode: one entry per sequence
     (2, 600, 1),     # several workgroups per sequence, second launch advances the lengths
@@ -577,3 +607,63 @@ def test_decode_group_step_small(csa, orc):
             else:
                 csa.sparse_attend(gc, dev(topk_prev), swa_g[l], qf.cuda(), out, SM)
             attn_close(host(out.float()), ref_o, name=f"step {step} layer {l}")
+
+
+# ------------------------------------------------------------------ the pages' magnitudes
+def _scaled_rows(cid, tag, n, width, case):
+    """Rows at the magnitudes the report gives for post-RoPE latents: largest
+    |x| near sqrt(512) = 22.6 (its bound) or 10 (what it observes), and a
+    saturating case whose outlier groups reach 4 x 2688, past the FP4 range
+    (ai.info "Main Findings")."""
+    x = synth.normal(cid, tag, (n, width)).astype(np.float32)
+    peak = {"bound": 22.6, "observed": 10.0, "outliers": 22.6}[case]
+    x = x * np.float32(peak) / np.maximum(np.abs(x).max(axis=1, keepdims=True), np.float32(1e-30))
+    if case == "outliers":
+        k = np.arange(n)
+        g = (k * 7) % (width // 16)
+        for j in range(16):  # one group per row lifted to |x| up to 4 x 2688
+            x[k, 16 * g + j] *= np.float32(4 * 2688 / 22.6) * np.float32(1.0 if (k[0] + j) % 3 else -1.0)
+        x[::5] *= np.float32(0.01)  # and small rows beside them
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ["bound", "observed", "outliers"])
+def test_magnitude_cases(csa, orc, case):
+    """Top-K, pool and attention over main KV, indexer K and window rows at the
+    pages' magnitudes.  Reports the largest absolute and relative attention
+    errors against the 2e-3 + 1e-2|ref| rule."""
+    B, E, S, Q = 2, 20000, 128, 1
+    cid = 40
+    cap = E + 4
+    oc = orc.Cache(B, cap, 1)
+    for b in range(B):
+        kv = _scaled_rows(cid, f"kv{b}{case}", E, 512, case)
+        oc.kv_codes[b, :E], oc.kv_scales[b, :E] = orc.quantize_main(kv)
+        k = _scaled_rows(cid, f"ik{b}{case}", E, 64, case)
+        oc.ik_codes[b, :E], oc.ik_scales[b, :E] = orc.quantize_ik(k)
+        oc.length[b] = E
+    iq = _scaled_rows(cid, f"iq{case}", B * Q * 4, 64, "bound").reshape(B, Q, 4, 64)
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+    gc = upload(csa, oc, with_main=True)
+    topk = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
+    pool = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.FULL, dev(iq), topk, pool_out=pool)
+    g_topk, g_pool = host(topk), host(pool)
+    swaps = 0
+    for b in range(B):
+        swaps += topk_swaps(g_topk[b, 0], ref_topk[b, 0], scores[b, 0], name=f"{case} b{b}")
+        swaps += pool_block_swaps(g_pool[b, 0], ref_pool[b, 0], scores[b, 0], E, name=f"{case} pool b{b}")
+    # window of the last 128 tokens at the same magnitudes (FP8 saturates at 448)
+    swa = np.zeros((B, S, 512), np.uint8)
+    for b in range(B):
+        x = _scaled_rows(cid, f"swa{b}{case}", 128, 512, case).reshape(1, 128, 512)
+        sub = np.zeros((1, S, 512), np.uint8)
+        orc.swa_append(sub, x, np.array([E], np.int32))
+        swa[b] = sub[0]
+    qf = bf16_round(_scaled_rows(cid, f"q{case}", B * Q * 16, 512, "observed").reshape(B, Q, 16, 512))
+    ref, _ = orc.attend(oc, g_topk, swa, qf.float().numpy(), SM)
+    out = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    csa.sparse_attend(gc, topk, dev(swa), qf.cuda(), out, SM)
+    mabs, mrel = attn_close(host(out.float()), ref, name=case)
+    print(f"magnitudes {case}: {swaps} boundary swaps; attention max abs {mabs:.2e}, max rel {mrel:.2e}, "
+          f"largest |ref| {np.abs(ref).max():.1f}")

@@ -3,8 +3,9 @@ the first leaves the encoder's ratio-2 entry pending, the second completes
 it), on a small batch and context, through the same Schedule38 class that
 bench.py times.  Every layer of both tokens is compared with the oracle's
 replay of the step: each indexing call's Top-K (and the pool) under the
-boundary rule, every attention output within 2e-3 + 1e-2|ref| where the two
-sides attended the same index set, and every cache byte after the step.
+boundary rule, every attention output within 2e-3 + 1e-2|ref| (over the GPU's
+own Top-K list where a boundary swap made the lists differ), and every cache
+byte after the step.
 """
 import numpy as np
 import pytest
@@ -25,9 +26,9 @@ def gpu():
     return csa
 
 
-# (sequences, context, sequences the oracle replays): two small cases compared
-# whole, and the benchmark's 16 x 128K workload sampled on its first sequence
-@pytest.mark.parametrize("B,ctx,hs", [(2, 4096, 2), (1, 40000, 1), (16, 131072, 1)])
+# (sequences, context, sequences the oracle replays): every sequence, up to the
+# benchmark's own 16 x 128K workload
+@pytest.mark.parametrize("B,ctx,hs", [(2, 4096, 2), (1, 40000, 1), (16, 131072, 16)])
 def test_schedule38_step(gpu, B, ctx, hs):
     print(f"schedule38 B={B} ctx={ctx}: building", flush=True)
     wl = bench.Schedule38(6, B, ctx, replicas=1, keep_host_seqs=hs)
@@ -35,7 +36,9 @@ def test_schedule38_step(gpu, B, ctx, hs):
     torch.cuda.synchronize()
     print("GPU step done, running the oracle", flush=True)
     ost = bench.OracleSchedule38(wl)
-    res = ost.step(want_scores=True)
+    gpu_used = [[np.ascontiguousarray(wl.used[t][l][:hs].cpu().numpy()) for l in range(len(bench.SCHEDULE38))]
+                for t in range(2)]
+    res = ost.step(want_scores=True, gpu_used=gpu_used)
     for n, c in wl.caches[0].items():
         oc = ost.oc[n]
         assert np.array_equal(c.length[:hs].cpu().numpy(), oc.length), n
@@ -59,19 +62,8 @@ def test_schedule38_step(gpu, B, ctx, hs):
                                               name=f"t{t} pool b{b}")
             got = wl.out[t][l].float().cpu().numpy()
             for b in range(hs):
-                # the oracle attends with its own Top-K; compare where the sets agree
-                if set(used[b, 0].tolist()) != set(r_topk(res[t], l)[b, 0].tolist()):
-                    continue
-                attn_close(got[b, 0], r["out"][b, 0], name=f"t{t} L{l} b{b}")
+                # out_cmp: the oracle's attention over the list the GPU attended with
+                attn_close(got[b, 0], r["out_cmp"][b, 0], name=f"t{t} L{l} b{b}")
                 compared += 1
-    print(f"schedule38 B={B} ctx={ctx}: {compared} of {2 * 38 * hs} attention outputs compared, "
-          f"{swaps} boundary swaps", flush=True)
-    assert compared >= 2 * 38 * hs - 4 * hs * 10  # nearly all: a swap changes one layer group at most
-
-
-def r_topk(res_t, l):
-    """The Top-K the oracle's layer l attended with: that of the latest indexing layer."""
-    for k in range(l, -1, -1):
-        if bench.SCHEDULE38[k][0] != "reuse":
-            return res_t[k]["topk"]
-    raise AssertionError("no indexing layer before layer 0")
+    print(f"schedule38 B={B} ctx={ctx}: {compared} attention outputs compared, {swaps} boundary swaps", flush=True)
+    assert compared == 2 * 38 * hs
