@@ -56,7 +56,8 @@ class CacheStruct(ctypes.Structure):
 
 
 EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_compress", "csa2_swa_append", "csa2_index_score_topk",
-           "csa2_sparse_attend", "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
+           "csa2_sparse_attend", "csa2_sparse_attend_noalloc", "csa2_workspace_bytes", "csa2_status_string",
+           "csa2_version")
 
 
 def _load(path):
@@ -77,6 +78,8 @@ def _load(path):
     L.csa2_index_score_topk.argtypes = [cp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.csa2_sparse_attend.restype = ctypes.c_int
     L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz, vp]
+    L.csa2_sparse_attend_noalloc.restype = ctypes.c_int
+    L.csa2_sparse_attend_noalloc.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp]
     L.csa2_workspace_bytes.restype = sz
     L.csa2_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32]
     L.csa2_status_string.restype = ctypes.c_char_p
@@ -280,3 +283,29 @@ def sparse_attend(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=Non
                                   _ptr(q), _ptr(q_pos), float(sm_scale), _ptr(out), _ptr(lse), Q, _ptr(ws),
                                   ws.numel() if ws is not None else 0, _stream(stream))
     _check(rc, "csa2_sparse_attend")
+
+
+def sparse_attend_noalloc(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=None, stream=None,
+                          swa_x=None, swa_len=None):
+    """csa2_sparse_attend_noalloc: sparse_attend with the split partials in the
+    library's own per-GPU device array (no workspace, no allocation)."""
+    Q = q.shape[1]
+    S = swa.shape[1]
+    _expect(q, torch.bfloat16, (cache.batch, Q, HEADS, D), "q")
+    _expect(out, torch.bfloat16, (cache.batch, Q, HEADS, D), "out")
+    _expect(topk, torch.int32, (cache.batch, Q, TOPK), "topk")
+    _expect(swa, torch.uint8, (cache.batch, S, D), "swa")
+    if lse is not None:
+        _expect(lse, torch.float32, (cache.batch, Q, HEADS), "lse")
+    if q_pos is not None:
+        _expect(q_pos, torch.int32, (cache.batch, Q), "q_pos")
+    T = 0
+    if swa_x is not None:
+        T = swa_x.shape[1]
+        _expect(swa_x, torch.float32, (cache.batch, T, D), "swa_x")
+        _expect(swa_len, torch.int32, (cache.batch,), "swa_len")
+    st = cache.struct()
+    rc = lib().csa2_sparse_attend_noalloc(ctypes.byref(st), _ptr(topk), _ptr(swa), S, _ptr(swa_x), _ptr(swa_len), T,
+                                          _ptr(q), _ptr(q_pos), float(sm_scale), _ptr(out), _ptr(lse), Q,
+                                          _stream(stream))
+    _check(rc, "csa2_sparse_attend_noalloc")

@@ -4,8 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "csa2.h"
 #include "kernels.hpp"
+
+// Device scratch of csa2_sparse_attend_noalloc: one array per GPU the library
+// runs on, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it only names the symbol); it looks up each
+// device's address once with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -42,6 +50,31 @@ csa2::LaunchCache to_launch(const csa2_cache* c) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_EHIP; }
+
+// This device's address of `scratch`, looked up on the first call that needs it
+// on the device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA2_EHIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return CSA2_EHIP;
+    if (sdev != dev) return CSA2_EINVAL;  // the stream must belong to the current device
+  }
+  if (dev < 0 || dev >= kMaxDevices) return CSA2_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
 
 // Debug library: a precondition violation that an earlier call's kernels
 // recorded on this device (read once the stream's earlier work is done) is
@@ -157,6 +190,25 @@ int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, uint8_t* sw
   if ((rc = device_status(stream)) != CSA2_OK) return rc;
   return from_hip(csa2::launch_attend(to_launch(cache), topk, swa, S, swa_x, swa_len, swa_T, q, q_pos, sm_scale, out,
                                       lse, Q, ws, (hipStream_t)stream));
+}
+
+int csa2_sparse_attend_noalloc(const csa2_cache* cache, const int32_t* topk, uint8_t* swa, int32_t S,
+                               const float* swa_x, const int32_t* swa_len, int32_t swa_T, const uint16_t* q,
+                               const int32_t* q_pos, float sm_scale, uint16_t* out, float* lse, int32_t Q,
+                               void* stream) {
+  // every host check first: a call that fails them touches no device
+  int rc = check_cache(cache, false, true);
+  if (rc != CSA2_OK) return rc;
+  if (Q < 0 || S < 1) return CSA2_EINVAL;
+  if (swa_x ? (swa_T < 1 || swa_T > S || !swa_len) : (swa_T != 0 || swa_len)) return CSA2_EINVAL;
+  if (cache->batch == 0 || (Q == 0 && !swa_x)) return CSA2_OK;
+  if (swa_x && (!swa || !aligned(swa, 16) || !aligned(swa_x, 16) || !aligned(swa_len, 4))) return CSA2_EINVAL;
+  const size_t need = Q > 0 ? csa2_workspace_bytes(CSA2_OP_ATTEND, cache->batch, Q, cache->capacity) : 0;
+  if (need > CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_EWORKSPACE;
+  void* ws = nullptr;
+  if ((rc = device_scratch(stream, &ws)) != CSA2_OK) return rc;
+  return csa2_sparse_attend(cache, topk, swa, S, swa_x, swa_len, swa_T, q, q_pos, sm_scale, out, lse, Q, ws,
+                            CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t capacity) {

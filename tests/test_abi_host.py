@@ -142,6 +142,23 @@ def test_compress_rejections(csa, L):
     assert c(p, p, 0, 4, 2, p, None) == csa.OK and c(p, p, 3, 0, 2, p, None) == csa.OK
 
 
+def test_attend_noalloc_rejections(csa, L):
+    """Host checks of the no-allocation attention call, all before any device use."""
+    p = ctypes.c_void_p(FAKE)
+    a = L.csa2_sparse_attend_noalloc
+    c = ctypes.byref(cache(csa, B=1, cap=100))
+    # 1,021 queries need two splits of partials, 64.1 MiB: more than the library's array
+    assert csa.workspace_bytes(csa.OP_ATTEND, 1, 1021, 100) > (64 << 20)
+    assert a(c, p, p, 128, None, None, 0, p, None, 0.1, p, None, 1021, None) == csa.EWORKSPACE
+    assert csa.workspace_bytes(csa.OP_ATTEND, 1, 1020, 100) <= (64 << 20)
+    assert csa.workspace_bytes(csa.OP_ATTEND, 1, 1025, 100) == 0
+    assert a(c, p, p, 0, None, None, 0, p, None, 0.1, p, None, 1, None) == csa.EINVAL      # S < 1
+    assert a(c, p, p, 128, p, None, 1, p, None, 0.1, p, None, 1, None) == csa.EINVAL      # swa_x without swa_len
+    assert a(c, p, p, 128, None, None, 0, p, None, 0.1, p, None, -1, None) == csa.EINVAL  # Q < 0
+    assert a(c, p, p, 128, None, None, 0, p, None, 0.1, p, None, 0, None) == csa.OK       # nothing to do
+    assert a(ctypes.byref(cache(csa, B=0)), p, p, 128, None, None, 0, p, None, 0.1, p, None, 1, None) == csa.OK
+
+
 def test_index_rejections(csa, L):
     p = ctypes.c_void_p(FAKE)
     f = L.csa2_index_score_topk
