@@ -39,6 +39,11 @@ SM_SCALE = float(np.float32(1.0 / math.sqrt(512.0)))
 ROWS_PER_SEQ = 1 << 22          # row namespace of one sequence in the seeded generators
 FILL_FLOATS = 32 * 1024 * 1024  # fp32 values per cache-fill chunk
 MAIN_ROW, IDX_ROW, SWA_ROW = 288, 68, 512
+# what the path computes in: E4M3 indexer keys and queries widened exactly to
+# bf16 on the matrix cores; FP4 E2M1 x E4M3-scale main rows and E4M3 window
+# rows widened exactly to fp16, with the bf16 query scaled exactly into fp16;
+# fp32 accumulation and softmax throughout
+DTYPE = "e4m3/e2m1 data; bf16 (indexer) and fp16 (attention) MFMA, fp32 accumulate"
 
 
 def log(*a):
@@ -175,6 +180,17 @@ class Workload:
             # the layer's window append runs inside its attention launch
             csa.sparse_attend(c, topk, swas[l], inp["q"][l], self.out[l], SM_SCALE, q_pos=self.q_pos,
                               ws=self.ws_att, swa_x=inp["x"][l], swa_len=seq)
+
+    def attend_layer(self, i):
+        """Layer 0's attention on replica i (its window append included)."""
+        inp = self.inputs[i]
+        seq = self.caches[i].length if (self.decode and self.r == 1) else self.seq_after
+        self.csa.sparse_attend(self.caches[i], self.topk[0], self.swas[i][0], inp["q"][0], self.out[0], SM_SCALE,
+                               q_pos=self.q_pos, ws=self.ws_att, swa_x=inp["x"][0], swa_len=seq)
+
+    def attend_bytes(self):
+        """Algorithmic bytes of one layer's attention: the gathered rows and the window."""
+        return self.B * self.Q * (512 * MAIN_ROW + 128 * SWA_ROW)
 
     def full_index(self, i):
         csa = self.csa
@@ -501,7 +517,7 @@ class OracleSchedule38:
         return res
 
 
-def cpu_baseline(wl, steps=2):
+def cpu_baseline(wl, steps=3):
     """The oracle, as it stands, on the first sequences of the same workload."""
     t0 = time.time()
     ost = OracleSchedule38(wl) if isinstance(wl, Schedule38) else OracleStep(wl)
@@ -627,6 +643,66 @@ def traffic_from_profiles(wl, kernel_name):
     return rec["hbm_bytes_per_launch"]
 
 
+def stream_ceiling(nbytes, reps=12, span=1 << 30, blocks=1024):
+    """The streaming-read ceiling over `nbytes` (the Full scan's size): a plain
+    non-temporal 16-byte-per-lane read kernel (libcsa2_roofline.so) over
+    windows rotated through `span` bytes, so that the 256 MB Infinity Cache
+    cannot serve a window twice in a row; a graph of `reps` reads, median of
+    10 replays.  Returns GB/s."""
+    import ctypes
+    import fp4_kv_cache_index_amd as csa
+    L = ctypes.CDLL(csa.ROOF_LIB_PATH)
+    f = L.csa2roof_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    nwin = max(3, span // max(nbytes, 1))
+    buf = torch.ones((nwin * nbytes) // 4 + 64, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def reads():  # on the stream current at the call (graph capture runs on its own)
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(reps):
+            rc = f(ctypes.c_void_p(buf.data_ptr() + (i % nwin) * nbytes), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                   blocks, sp)
+            assert rc == 0, rc
+    reads()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        reads()
+    ts = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3 / reps)
+    t = float(np.median(ts))
+    del buf
+    return nbytes / t / 1e9, t
+
+
+def time_calls(call, n, R):
+    """Mean and spread of `n` eager calls of call(i % R), each bracketed by HIP
+    events on the current stream and queued behind a sleep so that host launch
+    cost does not show."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(R):
+        call(i)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)  # keep the GPU busy while the launches queue up
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        call(i % R)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -743,19 +819,7 @@ def main():
         f"{step_gbps:.0f} GB/s on {step_bytes / 1e6:.1f} MB/step")
 
     # ---- dominant kernel: the Full indexer call, HIP events on its stream
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.roofline_iters)]
-    for i in range(R):
-        wl.full_index(i)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)  # keep the GPU busy while the launches queue up
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        wl.full_index(i % R)
-        b.record(stream)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    durs = time_calls(wl.full_index, args.roofline_iters, R)
     t_idx = float(np.mean(durs))
     E_idx = int(wl.caches[0].length.max().item()) if wl.decode else wl.ctx // wl.r
     # bytes: every indexer key of the batch once (the queries of a sequence share them);
@@ -791,6 +855,24 @@ def main():
                     launch_us_p10_p50_p90=pct([d * 1e6 for d in durs]))
         log(f"Full indexer call: {t_idx * 1e6:.1f} us, {tflops:.1f} TFLOP/s on {flops / 1e9:.2f} GFLOP")
 
+    # ---- the streaming-read ceiling over the same bytes, for the fraction of what a plain read reaches
+    if roof["bound"] == "hbm":
+        ceil_gbps, ceil_t = stream_ceiling(idx_bytes)
+        roof["ceiling_GBps"] = round(ceil_gbps, 1)
+        roof["frac_of_ceiling"] = round(roof["achieved"] / ceil_gbps, 4)
+        log(f"streaming-read ceiling over {idx_bytes / 1e6:.1f} MB: {ceil_gbps:.0f} GB/s ({ceil_t * 1e6:.1f} us)")
+    # ---- attention of one layer (attention launch + split merge), HIP events on its stream
+    roof_att = None
+    if hasattr(wl, "attend_layer"):
+        adurs = time_calls(wl.attend_layer, args.roofline_iters, R)
+        t_att = float(np.mean(adurs))
+        att_bytes = wl.attend_bytes()
+        achieved = att_bytes / t_att / 1e9
+        roof_att = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / PEAK_GBPS, 4), traffic=None,
+                        kernel="attend + merge (one csa2_sparse_attend call, layer 0)", bytes_per_launch=att_bytes,
+                        avg_launch_us=round(t_att * 1e6, 2), launch_us_p10_p50_p90=pct([d * 1e6 for d in adurs]))
+        log(f"attention layer: {t_att * 1e6:.1f} us, {achieved:.0f} GB/s on {att_bytes / 1e6:.2f} MB")
     if args.copy_calibration:
         copy_calibration()
     cpu = None
@@ -800,7 +882,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "step_us_p10_p50_p90": pct(step_us),
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context_tokens": wl.ctx, "ratio": wl.r,
                    "queries_per_seq": wl.Q, "group": list(wl.group), "replicas": R,
                    "hipgraph": graphs is not None, "steps_per_graph_launch": R if graphs is not None else 0},
@@ -808,7 +890,7 @@ def main():
         **({"tokens_per_step": 2, "csa2_bytes_per_token_per_sequence": round(step_bytes / 2 / wl.B)}
            if isinstance(wl, Schedule38) else {}),
         "step_frac_of_peak": round(step_gbps / PEAK_GBPS, 4),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "roofline_attention": roof_att, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 

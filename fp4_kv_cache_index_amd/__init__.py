@@ -39,6 +39,8 @@ EDEVICE = -6  # debug library: an earlier call found a device precondition viola
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 # the same library with the kernels' device-side precondition checks on
 DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2_debug.so")
+# measurement helper (the streaming-read ceiling), not part of the method
+ROOF_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2_roofline.so")
 _lib = None
 _debug_lib = None
 

@@ -9,6 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa2.so")
 DEBUG_LIB = os.path.join(HERE, "libcsa2_debug.so")
+ROOF_LIB = os.path.join(HERE, "libcsa2_roofline.so")
 SOURCES = ["quant_append.hip", "index.hip", "attend.hip", "csa2_abi.cpp"]
 HEADERS = ["codec.hpp", "kernels.hpp", "block_ops.hpp", "dev_check.hpp"]
 ARCH = "gfx950"
@@ -17,6 +18,20 @@ ARCH = "gfx950"
 def sources():
     return [os.path.join(CSRC, s) for s in SOURCES] + [os.path.join(CSRC, h) for h in HEADERS] + [
         os.path.join(INCLUDE, "csa2.h")]
+
+
+def build_roofline(verbose: bool = False) -> str:
+    """libcsa2_roofline.so: the streaming-read ceiling kernel the benchmark
+    reports the indexer scan against (a measurement helper, not the method)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-I", INCLUDE, "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(CSRC, "stream_ceiling.hip"), "-o", ROOF_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(ROOF_LIB + ".tmp", ROOF_LIB)
+    return ROOF_LIB
 
 
 def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
@@ -62,4 +77,5 @@ def build(verbose: bool = False, jobs: int = 4, debug: bool = False) -> str:
 if __name__ == "__main__":
     build(verbose=True)
     build(verbose=True, debug=True)
+    build_roofline(verbose=True)
     sys.exit(0)

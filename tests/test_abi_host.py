@@ -33,6 +33,27 @@ def test_exports_every_declared_symbol(csa):
         assert hasattr(L, s), s
 
 
+def test_roofline_helper_exports_its_header():
+    """libcsa2_roofline.so (the streaming-read ceiling helper) exports every
+    symbol include/csa2_roofline.h declares and rejects bad arguments before
+    touching a device."""
+    import fp4_kv_cache_index_amd as csa
+    src = open(os.path.join(ROOT, "include", "csa2_roofline.h")).read()
+    syms = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(csa2roof_\w+)\s*\(", src, re.M)))
+    assert syms == ["csa2roof_stream_read"]
+    L = ctypes.CDLL(csa.ROOF_LIB_PATH)
+    f = L.csa2roof_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    p = ctypes.c_void_p(FAKE)
+    assert f(None, 16, p, 1, None) == -1
+    assert f(p, 15, p, 1, None) == -1
+    assert f(ctypes.c_void_p(FAKE + 8), 16, p, 1, None) == -1
+    assert f(p, 16, None, 1, None) == -1
+    assert f(p, 16, p, 0, None) == -1
+    assert f(p, 0, p, 1, None) == 0
+
+
 def test_status_strings_and_version(csa):
     for code in (csa.OK, csa.EINVAL, csa.ECAPACITY, csa.EWORKSPACE, csa.EUNSUPPORTED, csa.EHIP, csa.EDEVICE):
         assert csa.status_string(code) and csa.status_string(code) != "unknown status"
