@@ -156,6 +156,7 @@ class Workload:
                                   device=dev)
         self.ws_att = torch.zeros(max(1, csa.workspace_bytes(csa.OP_ATTEND, B, Q, cap)), dtype=torch.uint8,
                                   device=dev)
+        self.fused_full = self.decode and self.r == 1 and self.group[0] in ("full", "full_pool")
         torch.cuda.synchronize()
 
     # one pass of the whole group on replica i
@@ -165,13 +166,21 @@ class Workload:
         if not self.decode:
             c.length.fill_(self.E_before)
         c.host_len_bound = self.E_before if not self.decode else c.host_len_bound
-        csa.quantize_append(c, inp["kv"], inp["ik"], logits=inp["lg"])
+        # a decode step at ratio 1 appends the Full layer's entry in its indexing call
+        fused = self.fused_full
+        if not fused:
+            csa.quantize_append(c, inp["kv"], inp["ik"], logits=inp["lg"])
         seq = c.length if (self.decode and self.r == 1) else self.seq_after
         topk = None
         for l, mode in enumerate(self.group):
             if mode in ("full", "full_pool"):
-                csa.index_score_topk(c, csa.FULL, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
-                                     pool_out=self.pool if mode == "full_pool" else None, ws=self.ws_idx)
+                pool = self.pool if mode == "full_pool" else None
+                if fused and l == 0:
+                    csa.append_index_score_topk(c, inp["kv"], inp["ik"], inp["iq"][l], self.topk[l], q_pos=self.q_pos,
+                                                pool_out=pool, ws=self.ws_idx)
+                else:
+                    csa.index_score_topk(c, csa.FULL, inp["iq"][l], self.topk[l], q_pos=self.q_pos, pool_out=pool,
+                                         ws=self.ws_idx)
                 topk = self.topk[l]
             elif mode == "reindex":
                 csa.index_score_topk(c, csa.REINDEX, inp["iq"][l], self.topk[l], q_pos=self.q_pos,
@@ -596,16 +605,21 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
         # the calibration copies are the last three device copies of the run
         return acc, [v for _, v in sorted(copies)[-3:]]
 
-    # the kernels of one Full call: score, filter (only the Full call launches it
-    # at this workload) and final (the Full call's has the larger grid: it also
-    # builds the pool)
+    # the kernels of one Full call.  Decode (one to three queries per sequence):
+    # index_head and index_select, Full instantiations (<false>; the select
+    # grid of the Full call is the larger: it also builds the pool).  More
+    # queries: score, filter (only the Full call launches it) and final.
     def full_call(acc, name, largest_grid=False):
         grids = [g for (n, g) in acc if name in n]
         return [v for (n, g), vals in acc.items()
                 if name in n and (not largest_grid or g == max(grids)) for v in vals]
 
-    parts = (("score", "index_score_kernel<4096, false>", False), ("filter", "index_filter_kernel", False),
-             ("final", "index_final_kernel", True))
+    head = synth.WORKLOADS[[k for k, w in synth.WORKLOADS.items() if w["name"] == workload_name][0]].get("Q", 1) < 4
+    if head:
+        parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false>", True))
+    else:
+        parts = (("score", "index_score_kernel<4096, false>", False), ("filter", "index_filter_kernel", False),
+                 ("final", "index_final_kernel", True))
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc, copy = per_kernel(path, counter)
@@ -620,7 +634,7 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
     for key in ("fetch", "write"):
         kib = sum(out[f"{key}_kib_{part}"] or 0.0 for part, _, _ in parts)
         tot += kib * 1024.0 * out[f"{key}_factor"]
-    src = "index.hip"
+    src = "index_head.hip" if head else "index.hip"
     sha = hashlib.sha256(open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", src), "rb").read()).hexdigest()
     out.update(source=src, source_sha256=sha, workload=workload_name, hbm_bytes_per_launch=round(tot))
     path = os.path.join(ROOT, "profiles", f"counters_index_full_{workload_name}.json")
@@ -835,7 +849,10 @@ def main():
         pairs = int(np.minimum(E_idx, (pos + 1) // wl.r).sum()) * wl.B
     flops = 2 * 4 * 64 * pairs
     traffic = traffic_from_profiles(wl, "index_full")
-    kernel_name = "index_score + index_filter + index_final (one csa2_index_score_topk Full call)"
+    if getattr(wl, "Q", 1) < 4:
+        kernel_name = "index_head + index_select (one csa2_index_score_topk Full call)"
+    else:
+        kernel_name = "index_score + index_filter + index_final (one csa2_index_score_topk Full call)"
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_GBPS * 1e9)  # FLOP per byte where the bf16 matrix cores take over
     if flops / idx_bytes < ridge:
         # decode (one or a few queries per sequence): bound by streaming the indexer keys

@@ -58,8 +58,8 @@ class CacheStruct(ctypes.Structure):
 
 
 EXPORTS = ("csa2_quantize_append", "csa2_quantize_append_proj", "csa2_compress", "csa2_swa_append", "csa2_index_score_topk",
-           "csa2_sparse_attend", "csa2_sparse_attend_noalloc", "csa2_workspace_bytes", "csa2_status_string",
-           "csa2_version")
+           "csa2_append_index_score_topk", "csa2_sparse_attend", "csa2_sparse_attend_noalloc",
+           "csa2_workspace_bytes", "csa2_status_string", "csa2_version")
 
 
 def _load(path):
@@ -78,6 +78,8 @@ def _load(path):
     L.csa2_swa_append.argtypes = [vp, i32, vp, vp, i32, i32, vp]
     L.csa2_index_score_topk.restype = ctypes.c_int
     L.csa2_index_score_topk.argtypes = [cp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.csa2_append_index_score_topk.restype = ctypes.c_int
+    L.csa2_append_index_score_topk.argtypes = [cp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.csa2_sparse_attend.restype = ctypes.c_int
     L.csa2_sparse_attend.argtypes = [cp, vp, vp, i32, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, vp, sz, vp]
     L.csa2_sparse_attend_noalloc.restype = ctypes.c_int
@@ -255,6 +257,33 @@ def index_score_topk(cache: Cache, mode, iq, topk_out, iw=None, q_pos=None, pool
                                      _ptr(topk_out), _ptr(pool_out), Q, _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream))
     _check(rc, "csa2_index_score_topk")
+
+
+def append_index_score_topk(cache: Cache, kv, ik, iq, topk_out, iw=None, q_pos=None, pool_out=None, ws=None,
+                            stream=None):
+    """csa2_append_index_score_topk: the Full layer's append of kv/ik ([B][T][512],
+    [B][T][64], ratio 1) and its scoring with Top-512 (and pool), in one call."""
+    T = kv.shape[1]
+    Q = iq.shape[1]
+    _expect(kv, torch.float32, (cache.batch, T, D), "kv")
+    _expect(ik, torch.float32, (cache.batch, T, IDX_DIM), "ik")
+    _expect(iq, torch.float32, (cache.batch, Q, IDX_HEADS, IDX_DIM), "iq")
+    _expect(topk_out, torch.int32, (cache.batch, Q, TOPK), "topk_out")
+    if iw is not None:
+        _expect(iw, torch.float32, (cache.batch, Q, IDX_HEADS), "iw")
+    if q_pos is not None:
+        _expect(q_pos, torch.int32, (cache.batch, Q), "q_pos")
+    if pool_out is not None:
+        _expect(pool_out, torch.int32, (cache.batch, Q, POOL), "pool_out")
+    need = workspace_bytes(OP_INDEX, cache.batch, Q, cache.capacity)
+    if ws is None and need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=iq.device)
+    st = cache.struct()
+    rc = lib().csa2_append_index_score_topk(ctypes.byref(st), _ptr(kv), _ptr(ik), T, cache.host_len_bound, _ptr(iq),
+                                            _ptr(iw), _ptr(q_pos), _ptr(topk_out), _ptr(pool_out), Q, _ptr(ws),
+                                            ws.numel() if ws is not None else 0, _stream(stream))
+    _check(rc, "csa2_append_index_score_topk")
+    cache.host_len_bound += T
 
 
 def sparse_attend(cache: Cache, topk, swa, q, out, sm_scale, lse=None, q_pos=None, ws=None, stream=None,

@@ -10,8 +10,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa2.so")
 DEBUG_LIB = os.path.join(HERE, "libcsa2_debug.so")
 ROOF_LIB = os.path.join(HERE, "libcsa2_roofline.so")
-SOURCES = ["quant_append.hip", "index.hip", "attend.hip", "csa2_abi.cpp"]
-HEADERS = ["codec.hpp", "kernels.hpp", "block_ops.hpp", "dev_check.hpp"]
+SOURCES = ["quant_append.hip", "index.hip", "index_head.hip", "attend.hip", "csa2_abi.cpp"]
+HEADERS = ["codec.hpp", "kernels.hpp", "block_ops.hpp", "dev_check.hpp", "quant_entry.hpp", "index_common.hpp"]
 ARCH = "gfx950"
 
 

@@ -150,6 +150,23 @@ __device__ __forceinline__ int block_scan_excl(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
+// block_scan_excl with one barrier: the caller writes tmp again only after
+// another barrier.
+__device__ __forceinline__ int block_scan_excl1(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  const int x = (int)wave_incl_scan((uint32_t)v);
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; w++) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
 // Exclusive offsets of v[0..n) (LDS) into off[] (LDS); returns the total.
 __device__ __forceinline__ int block_offsets(const int* v, int* off, int n, int* tmp) {
   int carry = 0;

@@ -83,7 +83,8 @@ int device_scratch(void* stream, void** out) {
 // GPU.
 int device_status(void* stream) {
   const hipStream_t s = (hipStream_t)stream;
-  const uint32_t e = csa2::take_append_dev_error(s) | csa2::take_index_dev_error(s) | csa2::take_attend_dev_error(s);
+  const uint32_t e = csa2::take_append_dev_error(s) | csa2::take_index_dev_error(s) | csa2::take_attend_dev_error(s) |
+                     csa2::take_head_dev_error(s);
   return e ? CSA2_EDEVICE : CSA2_OK;
 }
 
@@ -168,6 +169,35 @@ int csa2_index_score_topk(const csa2_cache* cache, int mode, const float* iq, co
                                      (hipStream_t)stream));
 }
 
+int csa2_append_index_score_topk(const csa2_cache* cache, const float* kv, const float* ik, int32_t T,
+                                  int32_t host_len_bound, const float* iq, const float* iw, const int32_t* q_pos,
+                                  int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  // the append's checks (ratio 1: no logits), then the Full call's
+  int rc = check_cache(cache, true, true);
+  if (rc != CSA2_OK) return rc;
+  if (cache->ratio != 1) return CSA2_EINVAL;
+  if (T < 0 || host_len_bound < 0 || Q < 0) return CSA2_EINVAL;
+  if ((int64_t)host_len_bound + T > cache->capacity) return CSA2_ECAPACITY;
+  if (cache->batch == 0 || (T == 0 && Q == 0)) return CSA2_OK;
+  if (T > 0 && (!kv || !ik || !aligned(kv, 16) || !aligned(ik, 4))) return CSA2_EINVAL;
+  if (Q > 0) {
+    if (!iq || !topk_out || !aligned(iq, 4) || !aligned(topk_out, 4)) return CSA2_EINVAL;
+    if ((iw && !aligned(iw, 4)) || (q_pos && !aligned(q_pos, 4)) || (pool_out && !aligned(pool_out, 4)))
+      return CSA2_EINVAL;
+    const size_t need = csa2_workspace_bytes(CSA2_OP_INDEX, cache->batch, Q, cache->capacity);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  }
+  if ((rc = device_status(stream)) != CSA2_OK) return rc;
+  const csa2::LaunchCache c = to_launch(cache);
+  if (Q == 0) return from_hip(csa2::launch_quant_append(c, kv, nullptr, ik, nullptr, T, (hipStream_t)stream));
+  if (T == 0)
+    return from_hip(csa2::launch_index(c, CSA2_FULL, iq, iw, q_pos, nullptr, topk_out, pool_out, Q, ws,
+                                       (hipStream_t)stream));
+  return from_hip(csa2::launch_append_index(c, kv, ik, T, iq, iw, q_pos, topk_out, pool_out, Q, ws,
+                                            (hipStream_t)stream));
+}
+
 int csa2_sparse_attend(const csa2_cache* cache, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
                        const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos, float sm_scale,
                        uint16_t* out, float* lse, int32_t Q, void* ws, size_t ws_bytes, void* stream) {
@@ -214,7 +244,7 @@ int csa2_sparse_attend_noalloc(const csa2_cache* cache, const int32_t* topk, uin
 size_t csa2_workspace_bytes(int op, int32_t B, int32_t Q, int32_t capacity) {
   if (B <= 0 || Q <= 0 || capacity < 0) return 0;
   const int64_t bq = (int64_t)B * Q;
-  if (op == CSA2_OP_INDEX) return csa2::index_ws_bytes(bq, capacity);
+  if (op == CSA2_OP_INDEX) return csa2::index_total_ws_bytes(bq, capacity);
   if (op == CSA2_OP_ATTEND) return csa2::attend_ws_bytes(bq);
   return 0;
 }

@@ -1,0 +1,1175 @@
+// Top-512 and candidate-pool selection of the CSA2 Full and Reindex layer
+// modes with the score keys kept on chip (DeepSeek-V4.1-Flash report:
+// technologiesdigest "CSA2" for the modes and Top-512; ai.info "Methodology in
+// Plain English" for the hierarchical pool: the first Full layer keeps the
+// 2,048 aligned 8-entry blocks whose largest index score ranks highest).
+// Used for one to three queries per sequence; more queries go through the
+// shared-load scorer in index.hip.
+//
+// Two kernels per call.
+//  1. index_head: W workgroups per query each score one share of the keys
+//     (Full: batches of 512 entries j, j + W, j + 2W, ... so that the query's
+//     workgroups stream one region together; Reindex: pool slots).  Each key
+//     becomes a u32 order key held in registers and counted in an LDS
+//     histogram of its top 12 bits.  At the end the workgroup finds in its
+//     histogram the bin that holds its own T-th largest key and writes every
+//     key in a higher bin (and the keys of that bin, unless they would pass the
+//     share's cap) to its own stretch of the query's candidate list as u64
+//     keys (score << 32 | ~id), with their count and the largest u64 key it
+//     did not write (its floor).  With a pool it does the same for the 8-entry
+//     block maxima.  With a fused append the workgroup whose batch holds a new
+//     entry first writes it to the cache.
+//  2. index_select: one workgroup per query and kind gathers the stretches
+//     and takes the K-th largest candidate S* (a histogram over the
+//     candidates' score range, then an exact rank inside the boundary bin).
+//     Every key any workgroup did not write is at most its floor, so when
+//     every floor is below S* the candidates at or above S* are the exact
+//     Top-K.  Otherwise (a share holding more of the Top-K than it wrote,
+//     e.g. clustered scores or wide ties) it re-scores that share with the
+//     same scoring core, adds its unwritten keys above S*, and selects again,
+//     until no floor is above S*.  The result is written in ascending order
+//     (the pool expanded to its entries) from a bitmap of the selected ids.
+//     Nothing in the workspace carries over from one call to the next.
+// Ties go to the lower index through the u64 key; the order is exact for any
+// input.
+#include <hip/hip_runtime.h>
+
+#include "block_ops.hpp"
+#include "codec.hpp"
+#include "dev_check.hpp"
+#include "index_common.hpp"
+#include "kernels.hpp"
+#include "quant_entry.hpp"
+
+namespace csa2 {
+
+constexpr int kFullIters = 9;     // most batches per workgroup, Full (their keys stay in registers)
+constexpr int kReindexIters = 2;  // batches per workgroup, Reindex (1,024 pool slots)
+constexpr int kResident = 512;    // head workgroups resident at once (two per compute unit)
+constexpr int kHeadCap = 8192;    // candidates per query and kind, summed over its workgroups
+
+// Workspace of the head path.  Workgroup j of a query writes its candidates
+// of each kind to its own stretch of the query's list, slots [j Tc, j Tc + n)
+// with Tc = kHeadCap / W, and n to count; nothing carries over between calls.
+struct HeadWs {
+  uint32_t* count;  // [BQ][2][wstride] candidates each workgroup wrote (entries or slots, blocks)
+  uint64_t* cand;   // [BQ][2][kHeadCap] u64 keys (score << 32 | ~id)
+  uint64_t* floor;  // [BQ][2][wstride] largest key a workgroup did not write (0: none)
+  uint32_t* cut;    // [BQ][2][wstride] its cut bin << 1 | whether that bin was written
+  int32_t* nvis;    // [BQ][2] entries visible to the query; length to store after a fused append (-1: none)
+  int32_t wstride;
+};
+
+// ------------------------------------------------------------------ geometry
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workgroups per query.  Reindex: 16 of 1,024 pool slots.  Full: every share
+// gets the same number of batches (at most kFullIters, whose keys stay in
+// registers), so the grid should fill whole rounds of the resident slots: the
+// fewest rounds that hold the shares needed, and as many shares as those
+// rounds hold.
+int head_workgroups(bool reindex, int32_t capacity, int64_t bq) {
+  if (reindex) return kPool / (kReindexIters * kBatchKeys);
+  const int64_t batches = ((int64_t)capacity + kBatchKeys - 1) / kBatchKeys;
+  const int64_t w_min = (batches + kFullIters - 1) / kFullIters;
+  if (bq < 1) bq = 1;
+  const int64_t rounds = (bq * w_min + kResident - 1) / kResident;
+  int64_t w = rounds * kResident / bq;
+  if (w < w_min) w = w_min;
+  if (w > batches) w = batches;
+  return (int)(w > 0 ? w : 1);
+}
+
+static inline int head_wmax(int32_t capacity, int64_t bq) {
+  const int a = head_workgroups(false, capacity, bq), b = head_workgroups(true, capacity, bq);
+  return a > b ? a : b;
+}
+
+size_t head_ws_bytes(int64_t bq, int32_t capacity) {
+  const int64_t W = head_wmax(capacity, bq);
+  return 256 + align256(bq * 2 * W * 4) + align256(bq * 2 * kHeadCap * 8) + align256(bq * 2 * W * 8) +
+         align256(bq * 2 * W * 4) + align256(bq * 2 * 4);
+}
+
+HeadWs head_ws_carve(void* ws, int64_t bq, int32_t capacity) {
+  const int64_t W = head_wmax(capacity, bq);
+  HeadWs w;
+  uint8_t* p = (uint8_t*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  w.count = (uint32_t*)p;
+  p += align256(bq * 2 * W * 4);
+  w.cand = (uint64_t*)p;
+  p += align256(bq * 2 * kHeadCap * 8);
+  w.floor = (uint64_t*)p;
+  p += align256(bq * 2 * W * 8);
+  w.cut = (uint32_t*)p;
+  p += align256(bq * 2 * W * 4);
+  w.nvis = (int32_t*)p;
+  w.wstride = (int32_t)W;
+  return w;
+}
+
+__device__ __forceinline__ uint64_t key64(uint32_t key, uint32_t id) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull); }
+
+// a key of a share is written to the candidates iff it is nonzero and its bin
+// is above the share's cut bin, or equal to it when that bin was written
+__device__ __forceinline__ bool head_written(uint32_t x, uint32_t cut) {
+  const uint32_t bn = x >> kBinShift, bt = cut >> 1;
+  return x != 0u && (bn > bt || (bn == bt && (cut & 1u)));
+}
+
+struct HeadLds {
+  uint32_t wmax[2][kScoreWaves];    // largest key of each wave, per kind
+  uint32_t cut[2];
+  int n[2];                         // keys written, per kind (zero before write_heads)
+  uint64_t wfloor[2][kScoreWaves];  // largest key each wave does not write, per kind
+};
+
+// One wave walks a kind's histogram down from the bin of the share's largest
+// key mx, 64 bins a step, to the bin bt where the count of keys at or above it
+// reaches T.  Returns the cut: bt << 1 | whether bin bt is written too (when
+// the keys above it and in it fit in T_cap; otherwise only the keys above it,
+// fewer than T, are written).  With fewer than T keys in all, every key is
+// written (cut = 0 << 1 | 1).
+__device__ uint32_t head_cut(const uint32_t* hist, uint32_t mx, int T, int T_cap) {
+  const int lane = threadIdx.x & 63;
+  int b_hi = mx ? (int)(mx >> kBinShift) : -1;
+  uint32_t above = 0u;
+  while (b_hi >= 0) {
+    const int bn = b_hi - lane;
+    const uint32_t cnt = bn >= 0 ? hist[bn] : 0u;
+    const uint32_t incl = wave_incl_scan(cnt);
+    const uint32_t tot = readlane(incl, 63);
+    if (above + tot >= (uint32_t)T) {
+      const uint64_t m = __ballot(above + incl >= (uint32_t)T);
+      const int l = __ffsll((unsigned long long)m) - 1;
+      const uint32_t il = __builtin_amdgcn_readlane(incl, l), cl = __builtin_amdgcn_readlane(cnt, l);
+      const uint32_t a = above + il - cl;  // keys in higher bins, fewer than T
+      return ((uint32_t)(b_hi - l) << 1) | ((a + cl <= (uint32_t)T_cap) ? 1u : 0u);
+    }
+    above += tot;
+    b_hi -= 64;
+  }
+  return 1u;
+}
+
+// Write a share's heads of `kinds` kinds (0: entries or pool slots, 1: block
+// maxima) to its own stretch of the query's candidate list (slots
+// [j T_cap, j T_cap + count) of each kind), with the count, the cut and the
+// floor: the largest key it did not write.  ks[kind][it]: this lane's key of
+// batch it (0 = none; a block key is held by lane 8b of its block only);
+// idf(kind, it): the key's id.  H.wmax holds every wave's largest key and H.n
+// is zero (the caller has synchronised after the histograms).  T: keys wanted,
+// T_cap: most keys a share may write.  Out-pointers are kind 0's; kind 1's
+// follow at `stride`.
+template <int kIters, typename IdF>
+__device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf, const uint32_t* hist0,
+                            const uint32_t* hist1, const int32_t (&T)[2], const int32_t (&T_cap)[2], int j,
+                            uint64_t* cand, uint32_t* count_out, uint64_t* floor_out, uint32_t* cut_out,
+                            int32_t stride, HeadLds& H) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int kind = 0; kind < 2; kind++) {
+    if (kind >= kinds) break;  // uniform
+    // every wave finds the same cut
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; w++) mx = max(mx, H.wmax[kind][w]);
+    const uint32_t cut = head_cut(kind ? hist1 : hist0, mx, T[kind], T_cap[kind]);
+    // this lane's written keys and the largest unwritten one
+    uint32_t mine = 0u;
+    uint64_t fl = 0ull;
+#pragma unroll
+    for (int it = 0; it < kIters; it++) {
+      const uint32_t x = ks[kind][it];
+      const bool w = head_written(x, cut);
+      mine += w ? 1u : 0u;
+      const uint64_t k = (x != 0u && !w) ? key64(x, idf(kind, it)) : 0ull;
+      fl = k > fl ? k : fl;
+    }
+    // one LDS atomic per wave reserves its slots in the share's stretch
+    uint32_t slot = (uint32_t)wave_alloc((int)mine, &H.n[kind]);
+    uint64_t* dst = cand + kind * kHeadCap + (int64_t)j * T_cap[kind];
+#pragma unroll
+    for (int it = 0; it < kIters; it++) {
+      const uint32_t x = ks[kind][it];
+      const bool w = head_written(x, cut);
+      if (w && slot < (uint32_t)T_cap[kind]) dst[slot] = key64(x, idf(kind, it));  // the cap always holds
+      slot += w ? 1u : 0u;
+    }
+    fl = wave_max(fl);
+    if (lane == 0) H.wfloor[kind][wave] = fl;
+    if (tid == 0) H.cut[kind] = cut;
+  }
+  __syncthreads();
+  if (tid < kinds) {
+    const int kind = tid;
+    uint64_t f = 0ull;
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; w++) f = max(f, H.wfloor[kind][w]);
+    floor_out[kind * stride] = f;
+    cut_out[kind * stride] = H.cut[kind];
+    count_out[kind * stride] = min((uint32_t)H.n[kind], (uint32_t)T_cap[kind]);
+  }
+}
+
+// ------------------------------------------------------------------ head kernel
+struct HeadArgs {
+  const uint8_t* ik_codes;
+  const float* ik_scales;
+  uint8_t* kv_codes_w;  // fused append: the cache planes it writes
+  uint8_t* kv_scales_w;
+  uint8_t* ik_codes_w;
+  float* ik_scales_w;
+  const int32_t* length;
+  int32_t cap, ratio;
+  const float* iq;
+  const float* iw;
+  const int32_t* q_pos;
+  const int32_t* pool_in;
+  int32_t Q;
+  int32_t W;          // workgroups per query
+  int32_t iters;      // batches per workgroup (at most kFullIters / kReindexIters)
+  int32_t blocks;     // Full: also the pool's block keys
+  int32_t T[2], T_cap[2];
+  const float* app_kv;  // fused append: [B][app_T][512] f32 new entries (ratio 1), or null
+  const float* app_ik;  // [B][app_T][64] f32
+  int32_t app_T;
+  HeadWs ws;
+};
+
+template <bool Reindex>
+__global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
+  constexpr int kIters = Reindex ? kReindexIters : kFullIters;
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_bhist[Reindex ? 1 : kBins];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q8[256];
+  __shared__ float s_c[4];
+  __shared__ HeadLds H;
+
+  const int64_t bq = blockIdx.x;
+  const int j = blockIdx.y;
+  const int Q = a.Q, W = a.W;
+  const int b = (int)(bq / Q), q = (int)(bq % Q);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the query element and head weight this thread quantises (threads 0-255),
+  // loaded first
+  const bool qthr = tid < 256;
+  const float iq_v = a.iq[bq * 256 + (tid & 255)];
+  const float iw_v = (a.iw && qthr) ? a.iw[bq * 4 + (tid >> 6)] : 1.0f;
+  // a fused append makes the new entries visible: the length in memory is the
+  // one before it (the select kernel advances it)
+  const int32_t len0 = a.length[b];
+  const bool fits = a.app_T > 0 && len0 >= 0 && (int64_t)len0 + a.app_T <= a.cap;
+  if (kDebug && j == 0 && q == 0 && tid == 0) {
+    if (len0 < 0 || len0 > a.cap)
+      dev_flag(kErrLength);
+    else if (a.app_T > 0 && !fits)
+      dev_flag(kErrCapacity);
+  }
+  const int32_t len = fits ? len0 + a.app_T : len0;
+  const int32_t p = a.q_pos ? a.q_pos[bq] : len * a.ratio - Q + q;
+  const int32_t n_vis = __builtin_amdgcn_readfirstlane(visible_count(len, a.cap, a.ratio, p));
+  if (j == 0 && tid == 0) {
+    a.ws.nvis[bq * 2] = n_vis;
+    a.ws.nvis[bq * 2 + 1] = fits ? len : -1;  // the length the select kernel stores
+  }
+  const int64_t row_base = (int64_t)b * a.cap;
+  const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
+
+  // ---- fused append: the new entries in this workgroup's batches, one wave each
+  if (!Reindex && fits) {
+    for (int t = wave; t < a.app_T; t += kScoreWaves) {  // wave-uniform
+      const int64_t e = (int64_t)len0 + t;
+      if ((e / kBatchKeys) % W != j || q != 0) continue;  // the first query's workgroup of that batch writes it
+      const float4* src = reinterpret_cast<const float4*>(a.app_kv + ((int64_t)b * a.app_T + t) * 512 + 8 * lane);
+      const float4 v0 = src[0], v1 = src[1];
+      const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const float k = a.app_ik[((int64_t)b * a.app_T + t) * 64 + lane];
+      quantize_store_entry(a.kv_codes_w, a.kv_scales_w, a.ik_codes_w, a.ik_scales_w, row_base + e, x, k, lane);
+    }
+    // the stores are complete before any wave of this workgroup loads those keys
+    // (__syncthreads waits for every store a thread has in flight)
+    __syncthreads();
+  }
+  // Every query's workgroups read a new entry: the other queries' workgroups of
+  // its batch are not the writer.  Decode calls have one query per sequence;
+  // with more, the queries after the first read the new entry only after the
+  // first query's workgroup has written it, which a launch does not order, so
+  // the host fuses the append only when Q == 1.
+
+  Scorer<Reindex> sc;
+  sc.init(a.ik_codes, a.ik_scales, row_base, n_vis);
+  int32_t pe[kIters][kBatch];
+  if constexpr (Reindex) {
+#pragma unroll
+    for (int it = 0; it < kIters; it++)
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) pe[it][jj] = pool[(int64_t)(j + it * W) * kBatchKeys + sc.key_of(jj)];
+    if (kDebug)
+      for (int it = 0; it < kIters; it++)
+        for (int jj = 0; jj < kBatch; jj++)
+          if (pe[it][jj] < -1 || pe[it][jj] >= n_vis) dev_flag(kErrPoolId);  // scored as absent
+  } else {
+#pragma unroll
+    for (int it = 0; it < kIters; it++)
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) pe[it][jj] = 0;
+  }
+  const int64_t n_keys = Reindex ? (int64_t)kPool : (int64_t)n_vis;  // keys of the query
+  auto base_of = [&](int it) -> int64_t { return (int64_t)(j + it * W) * kBatchKeys; };
+  auto live = [&](int it) -> bool { return it < a.iters && base_of(it) < n_keys; };  // uniform
+  BatchLoad ld[2];
+  if (live(0)) sc.issue(base_of(0), pe[0], ld[0]);
+  if (kIters > 1 && live(1)) sc.issue(base_of(1), pe[1], ld[1]);
+
+  for (int i = tid; i < kBins; i += kScoreThreads) {
+    s_hist[i] = 0u;
+    if (!Reindex && a.blocks) s_bhist[i] = 0u;
+  }
+  if (tid < 2) H.n[tid] = 0;
+  if (qthr) prep_query(iq_v, iw_v, s_q8, s_c, tid);
+  lds_barrier();  // LDS only: the first batch stays in flight
+  sc.load_query(s_q8, s_c);
+
+  uint32_t ks[2][kIters];  // this lane's entry (or slot) keys and block keys, per batch
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int it = 0; it < kIters; it++) {
+    ks[0][it] = 0u;
+    ks[1][it] = 0u;
+    if (!live(it)) continue;  // uniform; the later batches are past the keys too
+    if (it >= 1 && it + 1 < kIters && live(it + 1)) sc.issue(base_of(it + 1), pe[it + 1], ld[(it + 1) & 1]);
+    const int64_t k_own = base_of(it) + sc.own();
+    bool valid;
+    if constexpr (Reindex) {
+      const int32_t pj = sc.jl == 0 ? pe[it][0] : sc.jl == 1 ? pe[it][1] : sc.jl == 2 ? pe[it][2] : pe[it][3];
+      valid = pj >= 0 && pj < n_vis;
+    } else {
+      valid = k_own < n_vis;
+    }
+    const uint32_t key = sc.compute(ld[it & 1], valid);
+    ks[0][it] = key;
+    kmax = max(kmax, key);
+    if (key) atomicAdd(&s_hist[key >> kBinShift], 1u);
+    if (!Reindex && a.blocks) {
+      const uint32_t m = block_max8(key);
+      ks[1][it] = (lane & 7) == 0 ? m : 0u;  // held by the block's first lane
+      if ((lane & 7) == 0 && m) atomicAdd(&s_bhist[m >> kBinShift], 1u);
+    }
+  }
+  kmax = wave_max(kmax);  // the block keys' maximum is the same key
+  if (lane == 0) {
+    H.wmax[0][wave] = kmax;
+    H.wmax[1][wave] = kmax;
+  }
+  __syncthreads();  // the histograms and maxima are complete
+
+  const int64_t sl = (bq * 2) * a.ws.wstride + j;  // this share's floor and cut, kind 0
+  auto idf = [&](int kind, int it) -> uint32_t {  // entry or pool slot; block
+    const int64_t k = base_of(it) + sc.own();
+    return (uint32_t)(kind ? (k >> 3) : k);
+  };
+  const int kinds = (!Reindex && a.blocks) ? 2 : 1;
+  write_heads<kIters>(ks, kinds, idf, s_hist, s_bhist, a.T, a.T_cap, j, a.ws.cand + (bq * 2) * kHeadCap,
+                      a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.wstride, H);
+}
+
+// ------------------------------------------------------------------ select kernel
+struct SelectArgs {
+  const uint8_t* ik_codes;
+  const float* ik_scales;
+  int32_t* length;  // advanced here after a fused append
+  int32_t cap, ratio;
+  const float* iq;
+  const float* iw;
+  const int32_t* pool_in;
+  int32_t Q, W, iters, app_T;
+  int32_t tc;  // each workgroup's stretch of the candidate list (even, W tc <= kHeadCap)
+  // per kind: the slots of each stretch loaded before the counts are known (R,
+  // even, <= tc) and floor(2^32 / (R / 2)) + 1, so that p / (R / 2) ==
+  // umulhi(p, magic) for every p < kHeadCap / 2
+  int32_t spec[2];
+  uint32_t spec_magic[2];
+  HeadWs ws;
+  int32_t* topk_out;
+  int32_t* pool_out;
+};
+
+constexpr int kBitWords = 10240;  // the Full output bitmap: ids below 327,680
+
+struct SelectLds {
+  uint64_t set[kHeadCap];  // candidates (then the rank bitmap and its offsets)
+  union {
+    struct {
+      uint64_t out[kPoolBlocks];  // the selected keys; the boundary bin's keys during a selection
+      uint32_t idx[kPoolBlocks];  // each share's count while loading; ids in the wide-range output
+      uint32_t hist[kBins];       // candidates per bin of their score keys' range
+    };
+    uint32_t woff[kBitWords];  // Full Top-K output: the selected ids before each bitmap word
+  };
+  union {
+    uint32_t bits[kBitWords];  // one bit per selected id (Full)
+    struct {
+      int take[kBins / 2], off[kBins / 2], ge[kBins / 2];  // the wide-range output's buckets
+    };
+  };
+  SelShared sel;
+  uint8_t q8[256];
+  float c[4];
+  uint64_t wfl[kScoreWaves];
+  uint64_t wfm[kScoreWaves];  // largest floor of each wave's shares
+  int wj[kScoreWaves];
+  uint32_t wmx[kScoreWaves], wmn[kScoreWaves];
+  int wov[kScoreWaves];  // whether a wave's shares wrote more than the speculative slots
+  int tmp[16];
+  int n, n_out, n_tie, bt, above;
+  uint64_t kth;
+};
+
+// This thread's keys of L.set[0, n), i = tid + 512 r, loaded together (a load
+// and its use one after another would wait out the LDS latency per key); 0
+// past n (candidate keys are never 0).
+template <int N>
+struct KeyBatch {
+  static constexpr int kN = N;
+  uint64_t x[N];
+  __device__ __forceinline__ void load(const uint64_t* set, int n) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < N; r++) {
+      const uint64_t v = set[tid + r * kScoreThreads];  // inside L.set: N * 512 <= kHeadCap
+      x[r] = tid + r * kScoreThreads < n ? v : 0ull;
+    }
+  }
+};
+template <typename F>
+__device__ __forceinline__ void with_keys(const uint64_t* set, int n, F&& f) {
+  const int nr = (n + kScoreThreads - 1) / kScoreThreads;  // uniform
+  if (nr <= 4) {
+    KeyBatch<4> b;
+    b.load(set, n);
+    f(b);
+  } else if (nr <= 8) {
+    KeyBatch<8> b;
+    b.load(set, n);
+    f(b);
+  } else {
+    KeyBatch<kHeadCap / kScoreThreads> b;
+    b.load(set, n);
+    f(b);
+  }
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+__device__ __forceinline__ void set_bit(uint32_t* bits, uint32_t id) { atomicOr(&bits[id >> 5], 1u << (id & 31u)); }
+
+// The range [lo, hi] of the score keys (top 32 bits) of the n keys in L.set.
+// Every thread gets it.
+__device__ __forceinline__ void key_range(SelectLds& L, int n, uint32_t& lo, uint32_t& hi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  lo = ~0u;
+  hi = 0u;
+  with_keys(L.set, n, [&](auto& b) {
+#pragma unroll
+    for (int r = 0; r < b.kN; r++) {
+      const uint32_t x = (uint32_t)(b.x[r] >> 32);
+      lo = b.x[r] ? min(lo, x) : lo;
+      hi = max(hi, x);
+    }
+  });
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    L.wmx[wave] = hi;
+    L.wmn[wave] = lo;
+  }
+  __syncthreads();
+  lo = ~0u;
+  hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; w++) {
+    lo = min(lo, L.wmn[w]);
+    hi = max(hi, L.wmx[w]);
+  }
+  __syncthreads();
+}
+
+// The K-th largest S* of the n unique nonzero u64 keys in L.set (n > K),
+// whose score keys lie in [lo, hi]; with `mark`, also the bit of every key at
+// or above S* in L.bits (the key's id).  On entry L.hist and L.n_tie are zero
+// (and L.bits with `mark`); the call leaves them dirty.  The keys are counted
+// in 4,096 bins spanning [lo, hi]; a count over the bins from the top finds the
+// bin holding the K-th key; the keys of higher bins are taken, and that bin's
+// keys (typically one or two) are gathered and ranked exactly (by one wave when
+// there are at most 64 of them, else by the radix select).  Every thread gets
+// S*.
+__device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint32_t lo, uint32_t hi, bool mark) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kThr = kScoreThreads;
+  // bin of a score key: (x - lo) >> shift, with (hi - lo) >> shift below kBins
+  const uint32_t span = hi - lo;
+  const int shift = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 12));
+  with_keys(L.set, n, [&](auto& b) {
+#pragma unroll
+    for (int r = 0; r < b.kN; r++)
+      if (b.x[r]) atomicAdd(&L.hist[(((uint32_t)(b.x[r] >> 32)) - lo) >> shift], 1u);
+  });
+  __syncthreads();
+  {
+    // thread t counts bins [8c, 8c + 8) with c = kThr - 1 - t, so a prefix over
+    // the threads is a count from the top bin down; the thread whose range
+    // holds the K-th key finds its bin
+    constexpr int kPerT = kBins / kThr;
+    const int c = kThr - 1 - tid;
+    uint32_t h[kPerT];
+    uint32_t s = 0u;
+#pragma unroll
+    for (int u = 0; u < kPerT; u++) {
+      h[u] = L.hist[c * kPerT + u];
+      s += h[u];
+    }
+    int tot;
+    uint32_t acc = (uint32_t)block_scan_excl1((int)s, L.tmp, &tot);  // keys in higher bins
+    if (acc < (uint32_t)K && acc + s >= (uint32_t)K) {
+#pragma unroll
+      for (int u = kPerT - 1; u >= 0; u--) {
+        if (acc + h[u] >= (uint32_t)K) {
+          L.bt = c * kPerT + u;
+          L.above = (int)acc;
+          break;
+        }
+        acc += h[u];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t bt = (uint32_t)L.bt;
+  const int need = K - L.above;  // keys to take from the boundary bin, >= 1
+  // the keys of higher bins are taken; the boundary bin's are gathered
+  with_keys(L.set, n, [&](auto& b) {
+    int nt = 0;
+#pragma unroll
+    for (int r = 0; r < b.kN; r++) {
+      const uint32_t bn = (((uint32_t)(b.x[r] >> 32)) - lo) >> shift;
+      if (mark && b.x[r] && bn > bt) set_bit(L.bits, key_id(b.x[r]));
+      nt += (b.x[r] && bn == bt) ? 1 : 0;
+    }
+    int slot = wave_alloc(nt, &L.n_tie);
+#pragma unroll
+    for (int r = 0; r < b.kN; r++) {
+      const uint32_t bn = (((uint32_t)(b.x[r] >> 32)) - lo) >> shift;
+      if (b.x[r] && bn == bt) {
+        if (slot < kPoolBlocks) L.out[slot] = b.x[r];
+        slot++;
+      }
+    }
+  });
+  __syncthreads();
+  const int n_tie = L.n_tie;
+  if (n_tie <= 64) {
+    if (wave == 0) {  // rank by comparing every pair across the lanes
+      const uint64_t v = lane < n_tie ? L.out[lane] : 0ull;
+      int greater = 0;
+      for (int j = 0; j < n_tie; j++) greater += readlane(v, j) > v ? 1 : 0;
+      if (lane < n_tie && greater < need) {
+        if (mark) set_bit(L.bits, key_id(v));
+        if (greater == need - 1) L.kth = v;
+      }
+    }
+  } else {
+    if (n_tie <= kPoolBlocks && need < n_tie) {
+      int cnt;
+      const uint64_t t = topk_threshold<uint64_t>([&](int i) { return L.out[i]; }, n_tie, need, L.sel, &cnt);
+      if (tid == 0) L.kth = t;
+    } else if (n_tie <= kPoolBlocks) {  // the whole bin is taken: its smallest key
+      uint64_t m = ~0ull;
+      for (int i = tid; i < n_tie; i += kThr) m = min(m, L.out[i]);
+      m = wave_min(m);
+      if (lane == 0) L.wfl[wave] = m;
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t g = ~0ull;
+        for (int w = 0; w < kThr / 64; w++) g = min(g, L.wfl[w]);
+        L.kth = g;
+      }
+    } else {  // very wide ties: select over all keys
+      int cnt;
+      const uint64_t t = topk_threshold<uint64_t>([&](int i) { return L.set[i]; }, n, K, L.sel, &cnt);
+      if (tid == 0) L.kth = t;
+    }
+    if (mark) {  // the boundary bin's keys at or above S*
+      __syncthreads();
+      const uint64_t kth = L.kth;
+      with_keys(L.set, n, [&](auto& b) {
+#pragma unroll
+        for (int r = 0; r < b.kN; r++) {
+          const uint32_t bn = (((uint32_t)(b.x[r] >> 32)) - lo) >> shift;
+          if (b.x[r] && bn == bt && b.x[r] >= kth) set_bit(L.bits, key_id(b.x[r]));
+        }
+      });
+    }
+  }
+  __syncthreads();
+  return L.kth;  // not written again before two more barriers
+}
+
+// Re-score share j of query bq exactly as index_head did and append to L.set
+// every key of the kind that the share did not write and that is above s_star.
+template <bool Reindex>
+__device__ __forceinline__ void repair_share(const SelectArgs& a, int64_t bq, int kind, int j, uint32_t cut, uint64_t s_star,
+                             int32_t n_vis, SelectLds& L) {
+  const int b = (int)(bq / a.Q);
+  const int W = a.W;
+  const int lane = threadIdx.x & 63;
+  Scorer<Reindex> sc;
+  sc.init(a.ik_codes, a.ik_scales, (int64_t)b * a.cap, n_vis);
+  sc.load_query(L.q8, L.c);
+  const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
+  const int64_t n_keys = Reindex ? (int64_t)kPool : (int64_t)n_vis;
+  for (int it = 0; it < a.iters; it++) {
+    const int64_t base = (int64_t)(j + it * W) * kBatchKeys;
+    if (base >= n_keys) break;  // uniform
+    int32_t pe[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; jj++) pe[jj] = Reindex ? pool[base + sc.key_of(jj)] : 0;
+    BatchLoad ld;
+    sc.issue(base, pe, ld);
+    const int64_t k_own = base + sc.own();
+    bool valid;
+    if constexpr (Reindex) {
+      const int32_t pj = pe[sc.jl];
+      valid = pj >= 0 && pj < n_vis;
+    } else {
+      valid = k_own < n_vis;
+    }
+    uint32_t key = sc.compute(ld, valid);
+    uint32_t id = (uint32_t)k_own;
+    bool own = true;
+    if (kind == 1) {
+      key = block_max8(key);
+      id = (uint32_t)(k_own >> 3);
+      own = (lane & 7) == 0;
+    }
+    const uint64_t k64 = key64(key, id);
+    const bool add = own && key != 0u && !head_written(key, cut) && k64 > s_star;
+    const int slot = wave_slot(add, &L.n);
+    if (add && slot < kHeadCap) L.set[slot] = k64;
+  }
+  __syncthreads();
+}
+
+// grid (BQ, kinds): kind 0 writes the Top-512, kind 1 the candidate pool
+template <bool Reindex>
+__global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs a) {
+  __shared__ SelectLds L;
+  constexpr int kThr = kScoreThreads;
+  const int64_t bq = blockIdx.x;
+  const int kind = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = a.W, tc = a.tc;
+  const int K = kind ? kPoolBlocks : kTopK;
+  const int32_t n_vis = a.ws.nvis[bq * 2];
+  const uint64_t* cand = a.ws.cand + (bq * 2 + kind) * kHeadCap;
+  const uint32_t* counts = a.ws.count + (bq * 2 + kind) * a.ws.wstride;
+  const uint64_t* floors = a.ws.floor + (bq * 2 + kind) * a.ws.wstride;
+  const uint32_t* cuts = a.ws.cut + (bq * 2 + kind) * a.ws.wstride;
+  // ids of the output: entries or blocks (Full), pool slots (Reindex)
+  const int64_t universe = Reindex ? (int64_t)kPool : (kind == 0 ? (int64_t)n_vis : ((int64_t)n_vis + kBlock - 1) / kBlock);
+  const bool direct = !Reindex && universe <= 32 * (int64_t)kBitWords;  // uniform: the bitmap output
+  const int nw = direct ? (int)((universe + 31) >> 5) : 0;
+
+  // ---- the first R slots of every stretch (speculatively), the counts and the
+  // floors, all at once: thread t holds slot pairs p = t + 512 u (pair p is
+  // slots 2 (p mod R/2) and one more of stretch p div R/2), counts and floors of
+  // shares t + 512 f (W <= 2048)
+  constexpr int kPairs = kHeadCap / (2 * kThr);
+  constexpr int kFl = 4;
+  const int R = a.spec[kind], rh = R >> 1;
+  const uint32_t rh_magic = a.spec_magic[kind];
+  const uint32_t npairs = (uint32_t)W * (uint32_t)rh;
+  const BufRsrc cand_r = make_rsrc(cand, (uint32_t)W * (uint32_t)tc * 8u);
+  uint4 cv[kPairs];
+#pragma unroll
+  for (int u = 0; u < kPairs; u++) {
+    const uint32_t pp = (uint32_t)(tid + u * kThr);
+    const uint32_t sh = __umulhi(pp, rh_magic);
+    const uint32_t s0 = sh * (uint32_t)tc + 2u * (pp - sh * (uint32_t)rh);
+    cv[u] = buf_load16(cand_r, pp < npairs ? 8u * s0 : 0x80000000u);  // past the end: zeros, no access
+  }
+  const BufRsrc cn_r = make_rsrc(counts, (uint32_t)W * 4u);
+  const BufRsrc fl_r = make_rsrc(floors, (uint32_t)W * 8u);
+  uint32_t cn[kFl];
+  uint64_t fl[kFl];
+#pragma unroll
+  for (int f = 0; f < kFl; f++) {
+    cn[f] = __builtin_amdgcn_raw_buffer_load_b32(cn_r, 4u * (uint32_t)(tid + f * kThr), 0, 0);
+    fl[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(fl_r, 8u * (uint32_t)(tid + f * kThr), 0, 0));
+  }
+  // the histogram and the bitmap start clear
+  for (int i = tid; i < kBins; i += kThr) L.hist[i] = 0u;
+  for (int i = tid; i < nw; i += kThr) L.bits[i] = 0u;
+  uint64_t fmax = 0ull;
+  bool over = false;
+#pragma unroll
+  for (int f = 0; f < kFl; f++) {
+    if (tid + f * kThr < W) L.idx[tid + f * kThr] = cn[f];
+    fmax = max(fmax, fl[f]);
+    over = over || (int)cn[f] > R;  // zero past W
+  }
+  fmax = wave_max(fmax);
+  const bool wover = __ballot(over) != 0ull;
+  if (lane == 0) {
+    L.wfm[wave] = fmax;
+    L.wov[wave] = wover ? 1 : 0;
+  }
+  if (tid == 0) {
+    L.n = 0;
+    L.n_tie = 0;
+  }
+  __syncthreads();
+  // ---- the written slots into L.set, with the range of their score keys
+  {
+    uint64_t k[2 * kPairs];
+    bool v[2 * kPairs];
+    int nv = 0;
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < kPairs; u++) {
+      const uint32_t pp = (uint32_t)(tid + u * kThr);
+      const uint32_t sh = __umulhi(pp, rh_magic);
+      const int o = 2 * (int)(pp - sh * (uint32_t)rh);  // the pair's first slot in its stretch
+      const int c = sh < (uint32_t)W ? (int)L.idx[sh] : 0;
+      v[2 * u] = o < c;
+      v[2 * u + 1] = o + 1 < c;
+      k[2 * u] = ((uint64_t)cv[u].y << 32) | cv[u].x;
+      k[2 * u + 1] = ((uint64_t)cv[u].w << 32) | cv[u].z;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const uint32_t x = (uint32_t)(k[2 * u + h] >> 32);
+        nv += v[2 * u + h] ? 1 : 0;
+        lo = v[2 * u + h] ? min(lo, x) : lo;
+        hi = v[2 * u + h] ? max(hi, x) : hi;
+      }
+    }
+    int slot = wave_alloc(nv, &L.n);
+#pragma unroll
+    for (int i = 0; i < 2 * kPairs; i++)
+      if (v[i]) L.set[slot++] = k[i];
+    // stretches holding more than R keys: the rest, one wave per stretch
+    bool any_over = false;
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; w++) any_over = any_over || L.wov[w] != 0;
+    if (any_over) {  // uniform
+      for (int j = wave; j < W; j += kScoreWaves) {
+        const int c = (int)L.idx[j];
+        for (int o = R + lane; o - lane < c; o += 64) {  // wave-uniform trip count
+          const bool has = o < c;
+          const uint64_t x = has ? cand[(int64_t)j * tc + o] : 0ull;
+          const int so = wave_slot(has, &L.n);
+          if (has) {
+            L.set[so] = x;
+            lo = min(lo, (uint32_t)(x >> 32));
+            hi = max(hi, (uint32_t)(x >> 32));
+          }
+        }
+      }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      L.wmx[wave] = hi;
+      L.wmn[wave] = lo;
+    }
+  }
+  __syncthreads();
+  int n = L.n;
+  uint32_t lo = ~0u, hi = 0u;
+  uint64_t gfmax = 0ull;
+#pragma unroll
+  for (int w = 0; w < kScoreWaves; w++) {
+    lo = min(lo, L.wmn[w]);
+    hi = max(hi, L.wmx[w]);
+    gfmax = max(gfmax, L.wfm[w]);
+  }
+  // S* = 0 when every candidate is taken
+  uint64_t s_star = n > K ? select_kth(L, n, K, lo, hi, direct) : 0ull;
+  bool marked = n > K;  // the bitmap holds the selection
+
+  // ---- while a floor is above S*, repair the share with the largest and select again
+  if (gfmax > s_star) {
+    marked = false;
+    bool query_ready = false;
+    for (int round = 0; round < W; round++) {  // every round clears one share's floor
+      // the share with the largest floor above S* (lowest index on ties)
+      uint64_t best = 0ull;
+      int bj = -1;
+#pragma unroll
+      for (int f = 0; f < kFl; f++) {
+        const int jj = tid + f * kThr;
+        if (jj < W && fl[f] > s_star && fl[f] > best) {
+          best = fl[f];
+          bj = jj;
+        }
+      }
+      const uint64_t wbest = wave_max(best);
+      const uint64_t m = __ballot(best == wbest && bj >= 0);
+      int wj = -1;
+      if (m) wj = __builtin_amdgcn_readlane(bj, __ffsll((unsigned long long)m) - 1);
+      if (lane == 0) {
+        L.wfl[wave] = wbest;
+        L.wj[wave] = wj;
+      }
+      __syncthreads();
+      uint64_t gbest = 0ull;
+      int gj = -1;
+      for (int w = 0; w < kScoreWaves; w++)
+        if (L.wj[w] >= 0 && (L.wfl[w] > gbest || (L.wfl[w] == gbest && L.wj[w] < gj))) {
+          gbest = L.wfl[w];
+          gj = L.wj[w];
+        }
+      __syncthreads();
+      if (gj < 0) break;  // uniform: every floor is below S*
+      if (!query_ready) {
+        const int t = tid & 255;
+        const float qv = a.iq[bq * 256 + t];
+        const float wh = a.iw ? a.iw[bq * 4 + (t >> 6)] : 1.0f;
+        if (tid < 256) prep_query(qv, wh, L.q8, L.c, t);
+        __syncthreads();
+        query_ready = true;
+      }
+      // keep only the candidates at or above S*, then add share gj's unwritten keys above S*
+      if (n > K) {
+        if (tid == 0) L.n_out = 0;
+        __syncthreads();
+        for (int i0 = 0; i0 < n; i0 += kThr) {
+          const int i = i0 + tid;
+          const uint64_t x = i < n ? L.set[i] : 0ull;
+          const bool keep = i < n && x >= s_star;
+          const int so = wave_slot(keep, &L.n_out);
+          if (keep) L.out[so] = x;  // at most K kept
+        }
+        __syncthreads();
+        const int nk = L.n_out;
+        for (int i = tid; i < nk; i += kThr) L.set[i] = L.out[i];
+        if (tid == 0) L.n = nk;
+        __syncthreads();
+      }
+      repair_share<Reindex>(a, bq, kind, gj, cuts[gj], s_star, n_vis, L);
+      if (tid == 0 && L.n > kHeadCap) L.n = kHeadCap;  // never reached: at most K kept plus one share's keys
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < kFl; f++)
+        if (tid + f * kThr == gj) fl[f] = 0ull;
+      n = L.n;
+      if (n > K) {
+        for (int i = tid; i < kBins; i += kThr) L.hist[i] = 0u;
+        if (tid == 0) L.n_tie = 0;
+        key_range(L, n, lo, hi);  // synchronises after the clears
+        s_star = select_kth(L, n, K, lo, hi, false);
+      } else {
+        s_star = 0ull;
+      }
+    }
+    if (direct) {
+      for (int i = tid; i < nw; i += kThr) L.bits[i] = 0u;
+      __syncthreads();
+    }
+  }
+
+  constexpr int kR = kHeadCap / kThr;  // candidates per thread at most
+  if (direct) {
+    // ---- Full: one bit per selected id, then each thread writes the ids of its
+    // words in ascending order from its offset
+    if (!marked) {  // uniform
+      with_keys(L.set, n, [&](auto& b) {
+#pragma unroll
+        for (int r = 0; r < b.kN; r++)
+          if (b.x[r] && b.x[r] >= s_star) set_bit(L.bits, key_id(b.x[r]));  // ids below universe
+      });
+      __syncthreads();
+    }
+    // thread t owns words [N t, N t + N), contiguous so that its ids are one run
+    // of the ascending order, with N the least of 1, 2, 4, 8, 16, 20 that covers
+    // the bitmap; its words load together
+    auto emit = [&](auto tag) {
+      constexpr int N = decltype(tag)::value;
+      const int w0 = tid * N;
+      uint32_t wd[N];
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < N; i++) {
+        const uint32_t v = L.bits[w0 + i];  // inside L.bits: 512 N <= kBitWords
+        wd[i] = w0 + i < nw ? v : 0u;
+        cnt += __popc(wd[i]);
+      }
+      int nsel;
+      int pos = block_scan_excl1(cnt, L.tmp, &nsel);  // at most K set
+      if (kind == 0) {
+        // sparse: each selected id's rank is the selected ids before its word
+        // plus the set bits below it in the word
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+          if (w0 + i < nw) L.woff[w0 + i] = (uint32_t)pos;
+          pos += __popc(wd[i]);
+        }
+        __syncthreads();
+        int32_t* dst = a.topk_out + bq * kTopK;
+        with_keys(L.set, n, [&](auto& b) {
+#pragma unroll
+          for (int r = 0; r < b.kN; r++) {
+            if (b.x[r] && b.x[r] >= s_star) {
+              const uint32_t id = key_id(b.x[r]);
+              const uint32_t w = id >> 5;
+              const int rank = (int)L.woff[w] + __popc(L.bits[w] & ((1u << (id & 31u)) - 1u));
+              if (rank < kTopK) dst[rank] = (int32_t)id;
+            }
+          }
+        });
+        for (int i = nsel + tid; i < kTopK; i += kThr) dst[i] = -1;
+      } else {
+        // the chosen blocks in ascending order into L.idx, then each expanded to
+        // its visible entries (every chosen block is full except possibly the one
+        // holding the last visible entry, so block r of the order fills slots
+        // 8r .. 8r+7): thread t writes the int4 chunks t + 512 k
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+          uint32_t m = wd[i];
+          while (m) {
+            const int b = __ffs(m) - 1;
+            m &= m - 1u;
+            if (pos < kPoolBlocks) L.idx[pos] = (uint32_t)(32 * (w0 + i) + b);
+            pos++;
+          }
+        }
+        __syncthreads();
+        int4* po = reinterpret_cast<int4*>(a.pool_out + bq * kPool);
+#pragma unroll
+        for (int k = 0; k < 2 * kPoolBlocks / kThr; k++) {
+          const int c = tid + k * kThr;
+          const int p = c >> 1;
+          int4 v = make_int4(-1, -1, -1, -1);
+          if (p < nsel) {
+            const int e0 = (int)L.idx[p] * kBlock + 4 * (c & 1);
+            v = make_int4(e0 < n_vis ? e0 : -1, e0 + 1 < n_vis ? e0 + 1 : -1, e0 + 2 < n_vis ? e0 + 2 : -1,
+                          e0 + 3 < n_vis ? e0 + 3 : -1);
+          }
+          po[c] = v;
+        }
+      }
+    };
+    const int wpt = (nw + kThr - 1) / kThr;  // uniform
+    if (wpt <= 1)
+      emit(IntC<1>{});
+    else if (wpt <= 2)
+      emit(IntC<2>{});
+    else if (wpt <= 4)
+      emit(IntC<4>{});
+    else if (wpt <= 8)
+      emit(IntC<8>{});
+    else if (wpt <= 16)
+      emit(IntC<16>{});
+    else
+      emit(IntC<kBitWords / kScoreThreads>{});
+  } else {
+    // ---- the selected keys: every candidate at or above S*, one LDS atomic per wave
+    if (tid == 0) L.n_out = 0;
+    __syncthreads();
+    {
+      int nt = 0;
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        const int i = tid + r * kThr;
+        const uint64_t x = i < n ? L.set[i] : 0ull;
+        nt += (x != 0ull && x >= s_star) ? 1 : 0;
+      }
+      int so = wave_alloc(nt, &L.n_out);
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        const int i = tid + r * kThr;
+        const uint64_t x = i < n ? L.set[i] : 0ull;
+        if (x != 0ull && x >= s_star && so < kPoolBlocks) L.out[so++] = x;  // at most K taken
+      }
+    }
+    __syncthreads();
+    const int nsel = min(L.n_out, K);
+
+    // ---- ascending output.  Thread t holds the selected ids t + 512 j.  A
+    // Reindex id is a pool slot: the pool is ascending, so slot order is entry
+    // order, and the entry loads while the slots are ranked.
+    constexpr int kPer = kPoolBlocks / kThr;
+    const int per = K / kThr;
+    uint32_t id[kPer];
+    int32_t ent[kPer];
+#pragma unroll
+    for (int jj = 0; jj < kPer; jj++) {
+      const int i = tid + jj * kThr;
+      id[jj] = (jj < per && i < nsel) ? key_id(L.out[i]) : kNoId;
+    }
+    if (Reindex) {
+      const int32_t* pool = a.pool_in + bq * kPool;
+#pragma unroll
+      for (int jj = 0; jj < kPer; jj++) ent[jj] = pool[id[jj] != kNoId ? id[jj] : 0u];
+    }
+    uint32_t* bits = reinterpret_cast<uint32_t*>(L.set);  // the candidates are no longer needed
+    if (universe <= 32 * (int64_t)kRankWords) {
+      int rank[kPer];
+      rank_ids(id, universe, rank, bits, L.tmp);
+      if (kind == 0) {
+        int32_t* dst = a.topk_out + bq * kTopK;
+        if (id[0] != kNoId) dst[rank[0]] = Reindex ? ent[0] : (int32_t)id[0];
+        if (tid >= nsel) dst[tid] = -1;
+      } else {
+        int4* po = reinterpret_cast<int4*>(a.pool_out + bq * kPool);
+#pragma unroll
+        for (int jj = 0; jj < kPer; jj++) {
+          if (id[jj] == kNoId) continue;
+          int e[8];
+          const int base = (int)id[jj] * kBlock;
+#pragma unroll
+          for (int t = 0; t < 8; t++) e[t] = base + t < n_vis ? base + t : -1;
+          po[2 * rank[jj]] = make_int4(e[0], e[1], e[2], e[3]);
+          po[2 * rank[jj] + 1] = make_int4(e[4], e[5], e[6], e[7]);
+        }
+        for (int i = nsel + tid; i < kPoolBlocks; i += kThr) {
+          po[2 * i] = make_int4(-1, -1, -1, -1);
+          po[2 * i + 1] = make_int4(-1, -1, -1, -1);
+        }
+      }
+    } else {
+      // wide id ranges (Full only): bucketed ordering through LDS
+#pragma unroll
+      for (int jj = 0; jj < kPer; jj++)
+        if (id[jj] != kNoId) L.idx[tid + jj * kThr] = id[jj];
+      __syncthreads();
+      uint32_t* s_ord = reinterpret_cast<uint32_t*>(L.out);  // free once idx holds the ids
+      // entries of one 4,096-entry stretch share idx >> 12; blocks of one, idx >> 9
+      order_ascending(L.idx, nsel, kind ? 9 : 12, s_ord, bits, L.take, L.off, L.ge, L.tmp);
+      if (kind == 0) {
+        int4* dst = reinterpret_cast<int4*>(a.topk_out + bq * kTopK);
+        for (int i = tid; i < kTopK / 4; i += kThr) {
+          int4 v;
+          v.x = 4 * i + 0 < nsel ? (int)s_ord[4 * i + 0] : -1;
+          v.y = 4 * i + 1 < nsel ? (int)s_ord[4 * i + 1] : -1;
+          v.z = 4 * i + 2 < nsel ? (int)s_ord[4 * i + 2] : -1;
+          v.w = 4 * i + 3 < nsel ? (int)s_ord[4 * i + 3] : -1;
+          dst[i] = v;
+        }
+      } else {
+        int4* po = reinterpret_cast<int4*>(a.pool_out + bq * kPool);
+        for (int i = tid; i < kPoolBlocks; i += kThr) {
+          int e[8];
+          if (i < nsel) {
+            const int base = (int)s_ord[i] * kBlock;
+#pragma unroll
+            for (int t = 0; t < 8; t++) e[t] = base + t < n_vis ? base + t : -1;
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; t++) e[t] = -1;
+          }
+          po[2 * i] = make_int4(e[0], e[1], e[2], e[3]);
+          po[2 * i + 1] = make_int4(e[4], e[5], e[6], e[7]);
+        }
+      }
+    }
+  }
+  // ---- a fused append's length, once every kernel of the call that reads the old one is done
+  if (!Reindex && a.app_T > 0 && kind == 0 && (bq % a.Q) == 0 && tid == 0) {
+    const int32_t nl = a.ws.nvis[bq * 2 + 1];
+    if (nl >= 0) a.length[bq / a.Q] = nl;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+CSA2_DEV_ERROR_TAKER(take_head_dev_error)
+
+// per share: the keys wanted (one and a half times its even share of K, plus
+// 16) and the most it may write (the query's kHeadCap split evenly).  A share
+// holding more of the Top-K than it wrote is re-scored by the select kernel.
+static void head_targets(int W, int K, int32_t& T, int32_t& T_cap) {
+  T_cap = (kHeadCap / W) & ~1;  // even: the select kernel loads slot pairs
+  const int want = (3 * K + 2 * W - 1) / (2 * W) + 16;
+  T = want < T_cap ? want : T_cap;
+}
+
+hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq, const float* iw,
+                             const int32_t* q_pos, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
+                             int32_t Q, const float* app_kv, const float* app_ik, int32_t app_T, void* ws_head,
+                             hipStream_t stream) {
+  const int64_t bq = (int64_t)c.batch * Q;
+  if (bq == 0) return hipSuccess;
+  const int kinds = (!reindex && pool_out) ? 2 : 1;
+  HeadArgs h;
+  h.ik_codes = c.ik_codes;
+  h.ik_scales = c.ik_scales;
+  h.kv_codes_w = c.kv_codes;
+  h.kv_scales_w = c.kv_scales;
+  h.ik_codes_w = c.ik_codes;
+  h.ik_scales_w = c.ik_scales;
+  h.length = c.length;
+  h.cap = c.capacity;
+  h.ratio = c.ratio;
+  h.iq = iq;
+  h.iw = iw;
+  h.q_pos = q_pos;
+  h.pool_in = pool_in;
+  h.Q = Q;
+  h.W = head_workgroups(reindex, c.capacity, bq);
+  if (reindex) {
+    h.iters = kReindexIters;
+  } else {
+    const int64_t batches = ((int64_t)c.capacity + kBatchKeys - 1) / kBatchKeys;
+    h.iters = (int32_t)((batches + h.W - 1) / h.W);
+  }
+  h.blocks = kinds == 2 ? 1 : 0;
+  head_targets(h.W, kTopK, h.T[0], h.T_cap[0]);
+  head_targets(h.W, kPoolBlocks, h.T[1], h.T_cap[1]);
+  h.app_kv = app_kv;
+  h.app_ik = app_ik;
+  h.app_T = app_T;
+  h.ws = head_ws_carve(ws_head, bq, c.capacity);
+  const dim3 grid((unsigned)bq, (unsigned)h.W);
+  if (reindex)
+    hipLaunchKernelGGL(index_head_kernel<true>, grid, dim3(kScoreThreads), 0, stream, h);
+  else
+    hipLaunchKernelGGL(index_head_kernel<false>, grid, dim3(kScoreThreads), 0, stream, h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelectArgs s;
+  s.ik_codes = c.ik_codes;
+  s.ik_scales = c.ik_scales;
+  s.length = c.length;
+  s.cap = c.capacity;
+  s.ratio = c.ratio;
+  s.iq = iq;
+  s.iw = iw;
+  s.pool_in = pool_in;
+  s.Q = Q;
+  s.W = h.W;
+  s.iters = h.iters;
+  s.app_T = app_T;
+  s.tc = h.T_cap[0];
+  for (int k = 0; k < 2; k++) {
+    // twice the keys wanted covers a share's count but for a wide boundary bin
+    const int r = 2 * h.T[k] < s.tc ? 2 * h.T[k] : s.tc;
+    s.spec[k] = (r + 1) & ~1;
+    s.spec_magic[k] = (uint32_t)((1ull << 32) / (uint64_t)(s.spec[k] / 2) + 1ull);
+  }
+  s.ws = h.ws;
+  s.topk_out = topk_out;
+  s.pool_out = reindex ? nullptr : pool_out;
+  const dim3 sgrid((unsigned)bq, (unsigned)kinds);
+  if (reindex)
+    hipLaunchKernelGGL(index_select_kernel<true>, sgrid, dim3(kScoreThreads), 0, stream, s);
+  else
+    hipLaunchKernelGGL(index_select_kernel<false>, sgrid, dim3(kScoreThreads), 0, stream, s);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -45,6 +45,11 @@ struct IndexWs {
 int64_t index_slots(int32_t capacity);
 size_t index_ws_bytes(int64_t bq, int32_t capacity);
 IndexWs index_ws_carve(void* ws, int64_t bq, int32_t capacity);
+// the head path (index_head.hip): one to three queries per sequence, and Reindex
+size_t head_ws_bytes(int64_t bq, int32_t capacity);
+int head_workgroups(bool reindex, int32_t capacity, int64_t bq);
+// the index workspace holds both paths' regions: the shared-load path's first
+size_t index_total_ws_bytes(int64_t bq, int32_t capacity);
 
 // ---- attention geometry
 constexpr int kAttnKeys = 640;  // 512 selected + 128 window
@@ -63,6 +68,7 @@ enum : uint32_t {
 uint32_t take_append_dev_error(hipStream_t stream);
 uint32_t take_index_dev_error(hipStream_t stream);
 uint32_t take_attend_dev_error(hipStream_t stream);
+uint32_t take_head_dev_error(hipStream_t stream);
 
 hipError_t launch_quant_append(const LaunchCache& c, const float* kv, const float* logits, const float* ik,
                                const float* w_ik, int32_t T, hipStream_t stream);
@@ -73,6 +79,19 @@ hipError_t launch_compress(const float* kv, const float* logits, int32_t B, int3
 hipError_t launch_index(const LaunchCache& c, int mode, const float* iq, const float* iw, const int32_t* q_pos,
                         const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws,
                         hipStream_t stream);
+// One to three queries per sequence (Full) or Reindex: scoring with on-chip
+// candidates, then the exact selection.  With app_T > 0 (Full, ratio 1, one
+// query per sequence) the scoring launch first appends app_T new entries per
+// sequence (app_kv [B][app_T][512], app_ik [B][app_T][64]) and the selection
+// launch advances the lengths.
+hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq, const float* iw,
+                             const int32_t* q_pos, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
+                             int32_t Q, const float* app_kv, const float* app_ik, int32_t app_T, void* ws_head,
+                             hipStream_t stream);
+constexpr int kMaxFusedAppend = 8;  // new entries per sequence an indexing launch appends itself
+hipError_t launch_append_index(const LaunchCache& c, const float* kv, const float* ik, int32_t T, const float* iq,
+                               const float* iw, const int32_t* q_pos, int32_t* topk_out, int32_t* pool_out,
+                               int32_t Q, void* ws, hipStream_t stream);
 hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa, int32_t S, const float* swa_x,
                          const int32_t* swa_len, int32_t swa_T, const uint16_t* q, const int32_t* q_pos,
                          float sm_scale, uint16_t* out, float* lse, int32_t Q, void* ws, hipStream_t stream);

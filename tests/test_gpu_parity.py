@@ -329,8 +329,9 @@ def test_index_full_prefill_chunk_no_pool(csa, orc):
 # than the candidate buffer holds, selected inside the final kernel
 @pytest.mark.parametrize("E", [9000, 40000, 70000])
 def test_index_relu_zero_ties_exact(csa, orc, E):
-    """Every score is 0: all keys tie, more than the candidate buffer holds, so
-    the exact fallback that streams the keys decides by entry index."""
+    """Every score is 0: all keys tie in one histogram bin, more than any
+    workgroup may write, so the select kernel re-scores the workgroups whose
+    unwritten keys could still win and decides by entry index."""
     B = 1
     oc = orc.Cache(B, E, 1)
     k = np.abs(synth.normal_rows(22, "pos", 0, E, 64)) + 0.1
@@ -364,6 +365,90 @@ def test_index_weights_and_needles(csa, orc):
     topk_swaps(topk[0, 0], ref[0, 0], scores[0, 0])
     pool_block_swaps(pool[0, 0], ref_pool[0, 0], scores[0, 0], E)
     assert set(needles.tolist()) <= set(topk[0, 0].tolist())
+
+
+@pytest.mark.parametrize("lo,n_hot", [(0, 700), (30000, 2000), (61440, 4)])
+def test_index_clustered_scores_repair(csa, orc, lo, n_hot):
+    """High scores packed into consecutive entries, so that one or two scoring
+    workgroups hold more of the Top-512 (and of the pool's best blocks) than they
+    write as candidates: the select kernel must re-score them.  Full Top-512,
+    pool and Reindex over that pool against the oracle."""
+    B, E = 1, 62000
+    iq = synth.normal(27, f"iq{lo}", (1, 1, 4, 64))
+    k = synth.normal_rows(27, f"k{lo}", 0, E, 64) * np.float32(0.05)
+    direction = np.maximum(iq[0, 0], 0).sum(axis=0) + 1e-3
+    hot = np.arange(lo, min(E, lo + n_hot))
+    ramp = np.linspace(2.0, 3.0, len(hot), dtype=np.float32)[:, None]  # distinct scores
+    k[hot] = direction / np.abs(direction).max() * ramp
+    oc = orc.Cache(B, E, 1)
+    oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
+    oc.length[0] = E
+    ref, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq)
+    swaps = topk_swaps(topk[0, 0], ref[0, 0], scores[0, 0], name="full")
+    swaps += pool_block_swaps(pool[0, 0], ref_pool[0, 0], scores[0, 0], E, name="pool")
+    assert set(hot[:512].tolist()) <= set(topk[0, 0].tolist()) or len(hot) > 512
+    iq2 = synth.normal(27, f"iq2{lo}", (1, 1, 4, 64))
+    k2_ref, _, s2 = orc.index_topk(oc, orc.REINDEX, iq2, pool_in=ref_pool, want_scores=True)
+    rt = torch.empty((1, 1, 512), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.REINDEX, dev(iq2), rt, pool_in=dev(ref_pool))
+    swaps += topk_swaps(host(rt)[0, 0], k2_ref[0, 0], s2[0, 0], name="reindex")
+    # Reindex with the Full queries over a pool of the hot entries reproduces Full
+    rt2 = torch.empty((1, 1, 512), dtype=torch.int32, device="cuda")
+    csa.index_score_topk(gc, csa.REINDEX, dev(iq), rt2, pool_in=dev(ref_pool))
+    assert set(host(rt2)[0, 0].tolist()) == set(ref[0, 0].tolist())
+    print(f"clustered {lo}+{n_hot}: {swaps} boundary swaps")
+
+
+@pytest.mark.parametrize("B,E,T,Q,pool", [
+    (3, 9000, 1, 1, True),      # decode: the scoring launch appends the entry itself
+    (2, 40000, 3, 1, True),     # three new entries, no query before them
+    (2, 5000, 8, 1, False),     # the most entries appended inside the scoring launch
+    (2, 7000, 2, 2, True),      # two queries: the append runs as its own launch first
+    (2, 7000, 12, 1, True),     # twelve entries: likewise
+    (2, 7000, 0, 1, True),      # nothing to append
+])
+def test_append_index_fused_matches_separate(csa, orc, B, E, T, Q, pool):
+    """csa2_append_index_score_topk equals csa2_quantize_append followed by the
+    Full csa2_index_score_topk: every cache byte, the lengths, the Top-K and the
+    pool, and both match the oracle."""
+    cap = E + T + 4
+    oc = oracle_cache_ik(orc, B, cap, [E] * B, 28)
+    for b in range(B):
+        kv = synth.normal_rows(28, "kvpre", b * cap, E, 512)
+        oc.kv_codes[b, :E], oc.kv_scales[b, :E] = orc.quantize_main(kv)
+    kv_new = synth.normal(28, f"kv{T}", (B, T, 512)).astype(np.float32)
+    ik_new = synth.normal(28, f"ik{T}", (B, T, 64)).astype(np.float32)
+    iq = synth.normal(28, f"iq{T}{Q}", (B, Q, 4, 64))
+    outs = []
+    for fused in (False, True):
+        gc = upload(csa, oc, with_main=True)
+        topk = torch.empty((B, Q, 512), dtype=torch.int32, device="cuda")
+        po = torch.empty((B, Q, csa.POOL), dtype=torch.int32, device="cuda") if pool else None
+        if fused:
+            csa.append_index_score_topk(gc, dev(kv_new), dev(ik_new), dev(iq), topk, pool_out=po)
+        else:
+            if T:
+                csa.quantize_append(gc, dev(kv_new), dev(ik_new))
+            csa.index_score_topk(gc, csa.FULL, dev(iq), topk, pool_out=po)
+        torch.cuda.synchronize()
+        outs.append([host(t) for t in (gc.kv_codes, gc.kv_scales, gc.ik_codes, gc.ik_scales, gc.length, topk)] +
+                    ([host(po)] if pool else []))
+    for a, b_ in zip(*outs):
+        assert np.array_equal(a, b_)
+    # the oracle
+    if T:
+        orc.quantize_append(oc, kv_new, ik_new)
+    ref, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=pool, want_scores=True)
+    assert np.array_equal(outs[1][2], oc.ik_codes) and np.array_equal(outs[1][0], oc.kv_codes)
+    assert np.array_equal(outs[1][4], oc.length)
+    for b in range(B):
+        for q in range(Q):
+            topk_swaps(outs[1][5][b, q], ref[b, q], scores[b, q], name=f"b{b} q{q}")
+            if pool:
+                n_vis = int(oc.length[b]) - (Q - 1 - q)
+                pool_block_swaps(outs[1][6][b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
 
 
 @pytest.mark.parametrize("E", [3000, 16384, 50000])
