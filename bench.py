@@ -587,9 +587,11 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def summarize_counters(fetch_csv, write_csv, workload_name):
+def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
-    of `bench.py --copy-calibration` into HBM bytes per Full indexer call."""
+    of `bench.py --copy-calibration` into HBM bytes per Full indexer call.
+    head: whether the call runs the decode kernels (index_head + index_select);
+    by default, whether the workload has fewer than four queries per sequence."""
     import csv
     import hashlib
 
@@ -614,7 +616,8 @@ def summarize_counters(fetch_csv, write_csv, workload_name):
         return [v for (n, g), vals in acc.items()
                 if name in n and (not largest_grid or g == max(grids)) for v in vals]
 
-    head = synth.WORKLOADS[[k for k, w in synth.WORKLOADS.items() if w["name"] == workload_name][0]].get("Q", 1) < 4
+    if head is None:
+        head = next(w for w in synth.WORKLOADS.values() if w["name"] == workload_name).get("Q", 1) < 4
     if head:
         parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false>", True))
     else:

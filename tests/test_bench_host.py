@@ -22,8 +22,8 @@ def test_percentiles():
 
 
 def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
-    """The committed record's hash matches index.hip as it is, so its bytes are
-    reported; once the source differs the figure is withheld (None)."""
+    """The committed record's hash matches its kernel source as it is, so its
+    bytes are reported; once the source differs the figure is withheld (None)."""
     import bench
 
     class W:
@@ -31,12 +31,12 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
 
     rec = json.load(open(os.path.join(ROOT, "profiles", "counters_index_full_f_ri_2ru_b16_ctx128k.json")))
     assert bench.traffic_from_profiles(W, "index_full") == rec["hbm_bytes_per_launch"]
-    # a copy of the tree whose index.hip differs by one byte
+    # a copy of the tree whose measured source differs by one byte
     (tmp_path / "profiles").mkdir()
     (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
     (tmp_path / "profiles" / "counters_index_full_f_ri_2ru_b16_ctx128k.json").write_text(json.dumps(rec))
-    src = open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", "index.hip"), "rb").read()
-    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index.hip").write_bytes(src + b"\n")
+    src = open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", rec["source"]), "rb").read()
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / rec["source"]).write_bytes(src + b"\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.traffic_from_profiles(W, "index_full") is None
 
@@ -79,10 +79,45 @@ def test_counter_summary(tmp_path, monkeypatch):
     (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
     (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index.hip").write_bytes(b"// source\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    bench.summarize_counters(str(f), str(w), "wl_test")
+    bench.summarize_counters(str(f), str(w), "wl_test", head=False)
     out = json.load(open(tmp_path / "profiles" / "counters_index_full_wl_test.json"))
     assert abs(out["fetch_factor"] - 2.0) < 1e-12 and abs(out["write_factor"] - 1.0) < 1e-12
     assert out["fetch_kib_score"] == 70001.0 and out["fetch_kib_final"] == 600.0
     want = ((70001.0 + 5000.0 + 600.0) * 2.0 + (9500.0 + 600.0 + 1600.0)) * 1024
     assert out["hbm_bytes_per_launch"] == round(want)
     assert out["source"] == "index.hip" and len(out["source_sha256"]) == 64
+
+
+def test_counter_summary_decode_kernels(tmp_path, monkeypatch):
+    """The decode Full call: index_head plus the Full call's index_select (the
+    larger grid: Top-512 and pool); Reindex instantiations are left out."""
+    import bench
+    fields = "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+
+    def rows(counter, values):
+        return fields + "".join(f'{i},"{k}",{g},{counter},{v}\n' for i, (k, g, v) in enumerate(values))
+
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [("void csa2::index_head_kernel<false>(csa2::HeadArgs)", 262144, 70000.0),
+             ("void csa2::index_select_kernel<false>(csa2::SelectArgs)", 16384, 900.0),
+             ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 11000.0),
+             ("void csa2::index_select_kernel<true>(csa2::SelectArgs)", 8192, 600.0),
+             (copy, 65536, 131072.0), (copy, 65536, 131072.0), (copy, 65536, 131072.0)]
+    write = [("void csa2::index_head_kernel<false>(csa2::HeadArgs)", 262144, 800.0),
+             ("void csa2::index_select_kernel<false>(csa2::SelectArgs)", 16384, 1000.0),
+             ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 150.0),
+             (copy, 65536, 262144.0), (copy, 65536, 262144.0), (copy, 65536, 262144.0)]
+    f = tmp_path / "fetch.csv"
+    w = tmp_path / "write.csv"
+    f.write_text(rows("FETCH_SIZE", fetch))
+    w.write_text(rows("WRITE_SIZE", write))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index_head.hip").write_bytes(b"// source\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    bench.summarize_counters(str(f), str(w), "wl_test", head=True)
+    out = json.load(open(tmp_path / "profiles" / "counters_index_full_wl_test.json"))
+    assert out["fetch_kib_head"] == 70000.0 and out["fetch_kib_select"] == 900.0
+    want = ((70000.0 + 900.0) * 2.0 + (800.0 + 1000.0)) * 1024
+    assert out["hbm_bytes_per_launch"] == round(want)
+    assert out["source"] == "index_head.hip"
