@@ -7,35 +7,35 @@
 //
 // Key slots per query: 0..511 = the Top-512 list, 512..639 = window positions
 // p-127..p, taken in groups of 16.  A workgroup of four waves owns a range of
-// groups (a split); every wave runs its own groups start to finish, so the
-// key loop has no workgroup barrier:
-//   gather: lane l holds key l%16 of the group, channels 128(l/16)..+127
+// groups (a split) and takes them in blocks of four, one group per wave:
+//   gather: lane l holds key l%16 of its wave's group, channels 128(l/16)..+127
 //     (64 FP4 code bytes and 8 E4M3 scale bytes of a main row, or 128 bytes of
-//     a window row), as raw buffer loads issued one group ahead;
-//   dequantise in registers: v_cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the
-//     E2M1 values exactly and one fp16 multiply by the group scale gives
-//     x = code * scale, exact in fp16 (at most 6 significant bits, |x| in
-//     [2^-10, 2688]); window bytes widen exactly with v_cvt_scalef32_pk_f16_fp8;
+//     a window row), as raw buffer loads issued one block ahead;
+//   dequantise in registers, half a lane's channels at a time:
+//     v_cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the E2M1 values exactly
+//     and one fp16 multiply by the group scale gives x = code * scale, exact
+//     in fp16 (at most 6 significant bits, |x| in [2^-10, 2688]); window bytes
+//     widen exactly with v_cvt_scalef32_pk_f16_fp8;
 //   S^T = K Q^T on v_mfma_f32_16x16x32_f16 straight from those registers (key
 //     rows are the matrix rows, the 16 heads its columns; the contraction
-//     order of the 512 channels is permuted identically on both operands).
-//     The bf16 query is scaled per head by a power of two that puts its
-//     largest element in [2^14, 2^15), which makes its fp16 copy exact for
-//     every element within 2^-28 of the head's largest; the scores are scaled
-//     back exactly;
-//   softmax in fp32: lane l holds head l%16 for keys 4(l/16)..+3, which is
-//     the layout of the P^T operand of the next product, so P never leaves
-//     registers, and the running max, sum and rescaling are per lane;
-//   O^T += V^T P^T on v_mfma_f32_16x16x16_f16: the dequantised group goes to a
-//     per-wave LDS tile [key][channel] and comes back channel-major through
-//     the transposing read ds_read_b64_tr_b16.  O^T keeps head l%16 in lane l.
-// At the end the four waves' (max, sum, O) are combined through LDS.  With
-// one split the workgroup writes the bf16 output; with several it writes its
-// unnormalised fp32 partial and a second kernel merges the splits by their
-// maxima.  (Merging inside the launch would need the partials visible across
-// the XCDs' separate L2 caches: an agent-scope release writes back the L2 and
-// measured 40-90 us per launch on gfx950, against 1.9 us for a dependent
-// launch.)
+//     order of the 512 channels is permuted identically on both operands)
+//     against the query held in registers.  The bf16 query is scaled per head
+//     by a power of two that puts its largest element in [2^14, 2^15), which
+//     makes its fp16 copy exact for every element within 2^-28 of the head's
+//     largest; the scores are scaled back exactly;
+//   the four waves' scores (16 heads x 64 keys) and dequantised keys go to
+//     LDS; every wave takes the block's softmax for all 16 heads in fp32 (lane
+//     l holds head l%16 for 16 of the keys, the layout of the P^T operand of
+//     the next product), so all waves keep the same running max and sum;
+//   O^T = alpha O^T + V^T P^T on v_mfma_f32_16x16x32_f16 for the wave's own 128
+//     output channels, the keys coming back channel-major from the [key]
+//     [channel] tile through the transposing read ds_read_b64_tr_b16.
+// No combine across waves is needed at the end.  With one split the workgroup
+// writes the bf16 output; with several it writes its unnormalised fp32 partial
+// and a second kernel merges the splits by their maxima.  (Merging inside the
+// launch, the last split of a query merging, costs a counting atomic's round
+// trip and one compute unit reading every split's partial: measured slower
+// than the 1.9 us of a dependent launch on gfx950.)
 #include <hip/hip_runtime.h>
 
 #include "block_ops.hpp"
@@ -57,13 +57,11 @@ constexpr int kKeyGroup = 16;                      // keys per group (one MFMA t
 constexpr int kMainGroups = 512 / kKeyGroup;       // groups 0..31 hold Top-K slots, 32..39 the window
 constexpr int kVStride = 528;                      // fp16 per key row of a wave's V tile (512 + pad)
 constexpr int kQStride = 520;                      // fp16 per head row of the scaled query (512 + pad)
-constexpr int kXStride = 260;                      // fp32 per head row of the final exchange (256 + pad)
 constexpr int kFusedAppendMax = 8;  // new window tokens per sequence appended inside the attention launch
-static_assert(kWaves * 16 * kXStride * 4 <= kWaves * 16 * kVStride * 2, "exchange fits in the V tiles");
 
-// Splits per query (each a workgroup of four waves; groups per wave = 10 /
-// splits).  Few queries spread every query over 10 workgroups of one group per
-// wave, so that each workgroup gathers only 64 rows: a gather's time grows with
+// Splits per query (each a workgroup of four waves taking 10 / splits blocks
+// of 64 keys).  Few queries spread every query over 10 workgroups of one
+// block, so that each workgroup gathers only 64 rows: a gather's time grows with
 // the rows one compute unit fetches (measured on gfx950, 10,240 rows: 2.8 us at
 // 16 rows per workgroup, 4.0 at 64, 6.2 at 128).  Many queries fill the chip
 // with fewer splits and need no merge at all from 1,024 queries on.
@@ -238,9 +236,10 @@ __device__ __forceinline__ bool key_valid(const Wg& w, int grp, int32_t& id) {
 }
 
 // issue the loads of group grp (wave-uniform kind; no branch around a load)
-__device__ __forceinline__ void issue(const Wg& w, const AttnArgs& a, int grp, int32_t id, Raw& r) {
+__device__ __forceinline__ void issue(const Wg& w, const AttnArgs& a, int grp, int32_t id, Raw& r,
+                                      bool live = true) {
   const bool is_main = grp < kMainGroups;
-  const bool ok = key_valid(w, grp, id);
+  const bool ok = live && key_valid(w, grp, id);
   const int32_t pos = win_pos(w, grp);
   const uint32_t slot = (uint32_t)((pos >= 0 ? pos : 0) % a.S);
   const BufRsrc rr = is_main ? w.codes_r : w.swa_r;
@@ -315,319 +314,203 @@ __device__ __forceinline__ void stage_inputs(const Wg& w, const AttnArgs& a, con
   }
 }
 
-// This lane's quarter of key n of group grp as fp16 pairs: kh[c] holds
-// channels 128g + 2c, 2c + 1.  A window token appended by this call comes from s_new.
-__device__ __forceinline__ void dequant(const Wg& w, int grp, const Raw& r, const uint8_t* s_new, uint32_t (&kh)[64]) {
+// Half h of this lane's quarter of key n of group grp as fp16 pairs: kh[c]
+// holds channels 128g + 64h + 2c, 2c + 1 (c < 32).  A window token appended by
+// this call comes from s_new.
+__device__ __forceinline__ void dequant(const Wg& w, int grp, const Raw& r, const uint8_t* s_new, int h,
+                                             uint32_t (&kh)[32]) {
   if (grp < kMainGroups) {
-    const uint32_t scw[2] = {r.sc.x, r.sc.y};
+    const uint32_t scw = h ? r.sc.y : r.sc.x;
 #pragma unroll
-    for (int sg = 0; sg < 8; sg++) {  // scale group sg: channels 128g + 16sg .. +15
-      const uint32_t sb = (scw[sg >> 2] >> (8 * (sg & 3))) & 0xFFu;
+    for (int s4 = 0; s4 < 4; s4++) {  // scale group 4h + s4: channels 128g + 16(4h + s4) .. +15
+      const uint32_t sb = (scw >> (8 * s4)) & 0xFFu;
       const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb * 0x0101u, 1.0f, false);
-      const uint4 w4 = r.w[sg >> 1];
-      const uint32_t c0 = (sg & 1) ? w4.z : w4.x, c1 = (sg & 1) ? w4.w : w4.y;
-      fp4_word(c0, s2, kh + 8 * sg);
-      fp4_word(c1, s2, kh + 8 * sg + 4);
+      const uint4 w4 = r.w[2 * h + (s4 >> 1)];
+      const uint32_t c0 = (s4 & 1) ? w4.z : w4.x, c1 = (s4 & 1) ? w4.w : w4.y;
+      fp4_word(c0, s2, kh + 8 * s4);
+      fp4_word(c1, s2, kh + 8 * s4 + 4);
     }
   } else {
     const int32_t pos = win_pos(w, grp);
     const bool fresh = pos >= w.new_lo && pos < w.new_hi;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int j4 = 0; j4 < 4; j4++) {
+      const int j = 4 * h + j4;
       uint4 x = r.w[j];
       if (fresh) x = *reinterpret_cast<const uint4*>(s_new + (pos - w.new_lo) * 512 + 128 * w.g + 16 * j);
       const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        kh[8 * j + 2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
-        kh[8 * j + 2 * k + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, true));
+        kh[8 * j4 + 2 * k] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, false));
+        kh[8 * j4 + 2 * k + 1] = h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xw[k], 1.0f, true));
       }
     }
   }
 }
 
-// S^T = K Q^T for one group: st[i] = head n's (scaled) score of key 4g + i.
-// Step kb pairs channels 128g' + 8kb .. +7 of every quarter g' on both operands.
-__device__ __forceinline__ v4f score_group(const uint32_t (&kh)[64], const _Float16* s_q, int n, int g) {
-  v4f st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 16; kb++) {
-    const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
-    const v8h qb = *reinterpret_cast<const v8h*>(s_q + n * kQStride + 128 * g + 8 * kb);
-    st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, st, 0, 0, 0);
-  }
-  return st;
-}
-
-// the group's keys into a V tile [key][channel]: row n, channels 128g ..
-__device__ __forceinline__ void store_tile(const uint32_t (&kh)[64], _Float16* rows, int n, int g) {
-#pragma unroll
-  for (int c = 0; c < 16; c++)
-    *reinterpret_cast<uint4*>(rows + n * kVStride + 128 * g + 8 * c) =
-        make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
-}
-
-// Decode: one group of 16 keys per wave, 64 keys per workgroup, ten workgroups
-// (splits) per query.  The waves share their scores through LDS (16 heads x 64
-// keys), each takes the softmax over all 64, and wave w then owns output
-// channels 128w .. 128w+127 of P V over the workgroup's four dequantised key
-// groups, so the waves never combine output vectors.  Writes the unnormalised
-// fp32 partial and the (max, sum) per head.
 constexpr int kSStride = 68;  // fp32 per head row of the shared scores (64 keys + pad)
-__global__ void __launch_bounds__(kThreads) attend_decode_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_q[16 * kQStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // the 64 keys [key][channel]
+
+// More queries, fewer splits: a workgroup takes its split's groups in blocks
+// of four (64 keys), one group per wave, as the decode kernel takes its one
+// block, with an online softmax across the blocks.  Per block every wave
+// scores its group against the query (held in registers), shares the scores
+// and its dequantised keys through LDS, takes the softmax of the block for
+// all 16 heads (so every wave holds the same running max and sum), and
+// accumulates P V for its own 128 output channels: 32 accumulator registers
+// per lane, no combine at the end.  The next block's rows load while one is
+// processed.  The query staging area and the key tile share LDS, which keeps
+// the kernel under 80 KB: two workgroups per compute unit.
+template <int kGpw>  // blocks per workgroup
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) attend_block_kernel(AttnArgs a) {
+  static_assert(16 * kQStride <= kWaves * 16 * kVStride, "the query staging fits in the key tile");
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // query staging, then keys
   __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
   __shared__ float s_qfac[16];
-  const Wg w = make_wg(a, 1);
+  const Wg w = make_wg(a, kGpw);
   const int n = w.n, g = w.g, wave = w.wave;
-  const int grp = w.split * kWaves + wave;
+  // block j of this split: groups grp0 + 4j + wave
+  const int grp0 = w.split * kWaves * kGpw;
 
-  int32_t id = load_id(w, grp);
+  // Blocks go in pairs through a loop that is not unrolled, the rows of block
+  // j + 1 loading into the other register set while block j is processed; the
+  // loads past the last block are issued to offsets that read nothing, so no
+  // load sits under a branch.
+  int32_t id_a = load_id(w, grp0 + wave);
+  int32_t id_b = load_id(w, kGpw > 1 ? grp0 + kWaves + wave : kMainGroups);
   uint4 qraw[4];
   load_query(w, a, qraw);
   float2 xv[kFusedAppendMax];
   load_new(w, a, xv);
-  Raw r;
-  issue(w, a, grp, id, r);
+  Raw ra, rb;
+  issue(w, a, grp0 + wave, id_a, ra);
+  _Float16* s_q = s_v;  // staging: [head][kQStride]
   stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
   lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
   const float qfac = s_qfac[n];
-  const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id)) & 0xFFFFu;  // bit k: key k exists
+  v8h qb[16];  // the B operand of S^T = K Q^T: head n, channels 128g + 8kb .. +7
+#pragma unroll
+  for (int kb = 0; kb < 16; kb++) qb[kb] = *reinterpret_cast<const v8h*>(s_q + n * kQStride + 128 * g + 8 * kb);
+  lds_barrier();  // every wave holds its query operand: the staging area becomes the key tile
 
-  uint32_t kh[64];
-  dequant(w, grp, r, s_new, kh);
-  const v4f st = score_group(kh, s_q, n, g);
-  store_tile(kh, s_v + wave * 16 * kVStride, n, g);
-  {
-    v4f sc;
-#pragma unroll
-    for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
-    *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
-  }
-  lds_barrier();  // every wave's scores and keys are in
-
-  // ---------------- softmax of head n over the 64 keys: this lane holds keys 32kb + 8g .. +7
-  float sv[2][8];
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++) {
-    const v4f lo = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g);
-    const v4f hi = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g + 4);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      sv[kb][i] = lo[i];
-      sv[kb][4 + i] = hi[i];
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[kb][i]);
-  mx = rows_max(mx);
-  float ps = 0.0f;
-  v8h pb[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - mx);
-      ps += pv;
-      pb[kb][i] = (_Float16)pv;
-    }
-  ps = rows_sum(ps);
-
-  // ---------------- O^T = V^T P^T for channels 128 wave .. +127: tile ct, key block kb
-  v4f acc[8];
+  v4f acc[8];  // O^T: acc[c][i] = O[head n][channel 128 wave + 16c + 4g + i], relative to m_run
 #pragma unroll
   for (int c = 0; c < 8; c++) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++) {
-    const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-      const v4h lo = lds_read_tr16(vsrc + 16 * c);
-      const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
-      const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
-    }
-  }
-  // acc[c][i] = O[head n][channel 128 wave + 16c + 4g + i], relative to mx
-  float* po = a.part_o + ((int64_t)w.split * a.bq_total + w.bq) * 16 * 512 + n * 512 + 128 * wave + 4 * g;
-#pragma unroll
-  for (int c = 0; c < 8; c++) *reinterpret_cast<v4f*>(po + 16 * c) = acc[c];
-  if (wave == 0 && g == 0) {
-    float* pm = a.part_ml + ((int64_t)w.split * a.bq_total + w.bq) * 32;
-    pm[2 * n] = mx;
-    pm[2 * n + 1] = ps;
-  }
-}
-
-// Several groups per wave (more queries, fewer splits): every wave runs its
-// groups start to finish with an online softmax, the next group's rows in
-// flight while one is processed, and the four waves' (max, sum, O) are
-// combined through LDS at the end.  One split writes the bf16 output, several
-// their fp32 partials.
-template <int kGpw>  // groups per wave
-__global__ void __launch_bounds__(kThreads) attend_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_q[16 * kQStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // V tiles, then the exchange
-  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];  // new window tokens, E4M3
-  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-  __shared__ float s_qfac[16];
-
-  const Wg w = make_wg(a, kGpw);
-  const int n = w.n, g = w.g, wave = w.wave, tid = w.tid;
-  const int64_t bq = w.bq;
-  const int split = w.split;
-  // this wave's groups: grp0 .. grp0 + kGpw - 1
-  const int grp0 = (split * kWaves + wave) * kGpw;
-
-  // ---------------- ids first, then the query and the new window tokens, then the first rows
-  int32_t ids[kGpw + 2];  // two spare slots: the prefetch indices below stay in bounds
-  ids[0] = load_id(w, grp0);
-  if constexpr (kGpw > 1) ids[1] = load_id(w, grp0 + 1);
-  uint4 qraw[4];
-  load_query(w, a, qraw);
-  float2 xv[kFusedAppendMax];
-  load_new(w, a, xv);
-  Raw raw[2];
-  issue(w, a, grp0, ids[0], raw[0]);
-  stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
-  lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
-  const float qfac = s_qfac[n];
-
-  v4f acc[32];  // O^T: acc[ct][i] = O[head n][channel 16ct + 4g + i]
-#pragma unroll
-  for (int ct = 0; ct < 32; ct++) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  _Float16* vt = s_v + wave * 16 * kVStride;
 
-#pragma unroll
-  for (int gi = 0; gi < kGpw; gi++) {
-    const int grp = grp0 + gi;
-    Raw& r = raw[gi & 1];
-    // the next group's rows (its id loaded a group ago), and the id after it
-    if (gi + 1 < kGpw) {
-      if (gi + 2 < kGpw) ids[gi + 2] = load_id(w, grp0 + gi + 2);
-      issue(w, a, grp + 1, ids[gi + 1], raw[(gi + 1) & 1]);
-    }
-    int32_t id_c = ids[gi];
+  // block j: its rows in cur, its id id_c; issues block j + 1's rows (id id_n)
+  // into nxt and returns block j + 2's id
+  auto block = [&](int j, Raw& cur, Raw& nxt, int32_t id_c, int32_t id_n) -> int32_t {
+    const int grp = grp0 + kWaves * j + wave;
+    const int32_t id_n2 = load_id(w, j + 2 < kGpw ? grp + 2 * kWaves : kMainGroups);
+    issue(w, a, grp + kWaves, id_n, nxt, j + 1 < kGpw);
     const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id_c)) & 0xFFFFu;  // bit k: key k exists
+    // the group's keys in two halves of each lane's 128 channels: dequantise,
+    // score and store each half into the tile (free once every wave is past
+    // the previous block), so only one half is held in registers
+    if (j > 0) lds_barrier();  // every wave is done with the previous block's tile and scores
+    v4f st = {0.f, 0.f, 0.f, 0.f};
+    _Float16* rows = s_v + wave * 16 * kVStride + n * kVStride + 128 * g;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      uint32_t kh[32];
+      dequant(w, grp, cur, s_new, h, kh);
+#pragma unroll
+      for (int kb = 0; kb < 8; kb++) {
+        const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
+        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[8 * h + kb], st, 0, 0, 0);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; c++)
+        *reinterpret_cast<uint4*>(rows + 64 * h + 8 * c) = make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
+    }
+    {
+      v4f sc;
+#pragma unroll
+      for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
+      *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
+    }
+    lds_barrier();  // every wave's scores and keys are in
 
-    uint32_t kh[64];
-    dequant(w, grp, r, s_new, kh);
-    const v4f st = score_group(kh, s_q, n, g);
-    store_tile(kh, vt, n, g);
-
-    // ---------------- online softmax: st[i] is head n, key 4g + i
-    float s[4];
+    // ---- softmax of head n over the block: this lane holds keys 32kb + 8g .. +7
+    float sv[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      const v4f lo = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g);
+      const v4f hi = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g + 4);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        sv[kb][i] = lo[i];
+        sv[kb][4 + i] = hi[i];
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      s[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[kb][i]);
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
-    v4h pk;
     float ps = 0.0f;
+    v8h pb[2];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float pv = (s[i] == -INFINITY) ? 0.0f : __expf(s[i] - m_new);
-      ps += pv;
-      pk[i] = (_Float16)pv;
-    }
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - m_new);
+        ps += pv;
+        pb[kb][i] = (_Float16)pv;
+      }
     ps = rows_sum(ps);
     m_run = m_new;
     l_run = alpha * l_run + ps;
-    lds_wave_sync();  // the V tile is written
 
-    // ---------------- O^T = alpha O^T + V^T P^T, one 16-channel tile ct at a time
-    const _Float16* vsrc = vt + (4 * g + (n >> 2)) * kVStride + 4 * (n & 3);
+    // ---- O^T = alpha O^T + V^T P^T for channels 128 wave .. +127 (alpha = 1 before the first block)
 #pragma unroll
-    for (int ct = 0; ct < 32; ct++) {
-      const v4h va = lds_read_tr16(vsrc + 16 * ct);
-      if (gi > 0) {  // nothing accumulated before the first group
+    for (int c = 0; c < 8; c++) acc[c] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[ct][i] *= alpha;
-      }
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pk, acc[ct], 0, 0, 0);
-    }
-    lds_wave_sync();  // the tile is read before the next group overwrites it
-  }
-
-  // ---------------- combine the four waves: max and sum per head, then O
-  if (g == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_run;
-  }
-  lds_barrier();  // every wave is past its key loop: the V tiles are free
-  // this wave's weight for head n: exp(its max - the workgroup's max)
-  float M = -INFINITY;
+    for (int kb = 0; kb < 2; kb++) {
+      const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
 #pragma unroll
-  for (int w = 0; w < kWaves; w++) M = fmaxf(M, s_m[w][n]);
-  const float own = m_run == -INFINITY ? 0.0f : __expf(m_run - M);
-  float* sx = reinterpret_cast<float*>(s_v);  // [wave][head][kXStride]
-  const int oh = tid >> 4, oc = 16 * (tid & 15);  // combine: head oh, channels oc .. oc+15 of the half
-  // the workgroup's max and sum for head oh
-  float Lh = 0.0f, Mh = -INFINITY;
-  {
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) Mh = fmaxf(Mh, s_m[w][oh]);
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-      const float mw = s_m[w][oh];
-      Lh += (mw == -INFINITY ? 0.0f : __expf(mw - Mh)) * s_l[w][oh];
-    }
-  }
-#pragma unroll
-  for (int half = 0; half < 2; half++) {
-#pragma unroll
-    for (int c = 0; c < 16; c++) {
-      const int ct = 16 * half + c;
-      const v4f v = acc[ct] * own;
-      *reinterpret_cast<v4f*>(sx + (wave * 16 + n) * kXStride + 16 * c + 4 * g) = v;
-    }
-    lds_barrier();
-    float o[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) o[k] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-#pragma unroll
-      for (int k4 = 0; k4 < 4; k4++) {
-        const v4f v = *reinterpret_cast<const v4f*>(sx + (w * 16 + oh) * kXStride + oc + 4 * k4);
-#pragma unroll
-        for (int i = 0; i < 4; i++) o[4 * k4 + i] += v[i];
+      for (int c = 0; c < 8; c++) {
+        const v4h lo = lds_read_tr16(vsrc + 16 * c);
+        const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
+        const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
       }
     }
-    const int ch = 256 * half + oc;  // first output channel of this thread
-    if (a.splits == 1) {
-      const float inv = Lh > 0.0f ? 1.0f / Lh : 0.0f;
-      uint32_t pk2[8];
-#pragma unroll
-      for (int k = 0; k < 8; k++)
-        pk2[k] = (uint32_t)f32_to_bf16_rne(o[2 * k] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * k + 1] * inv) << 16);
-      uint4* dst = reinterpret_cast<uint4*>(a.out + (bq * 16 + oh) * 512 + ch);
-      dst[0] = make_uint4(pk2[0], pk2[1], pk2[2], pk2[3]);
-      dst[1] = make_uint4(pk2[4], pk2[5], pk2[6], pk2[7]);
-    } else {
-      float4* dst = reinterpret_cast<float4*>(a.part_o + (((int64_t)split * a.bq_total + bq) * 16 + oh) * 512 + ch);
-#pragma unroll
-      for (int k4 = 0; k4 < 4; k4++) dst[k4] = make_float4(o[4 * k4], o[4 * k4 + 1], o[4 * k4 + 2], o[4 * k4 + 3]);
+    return id_n2;
+  };
+#pragma unroll 1
+  for (int j = 0; j < kGpw; j += 2) {
+    const int32_t id_c = block(j, ra, rb, id_a, id_b);  // block j + 2's id
+    if (kGpw % 2 == 0 || j + 1 < kGpw) {  // always, for an even block count
+      const int32_t id_d = block(j + 1, rb, ra, id_b, id_c);
+      id_a = id_c;
+      id_b = id_d;
     }
-    if (half == 0) lds_barrier();  // the exchange is read before the second half overwrites it
   }
-  if ((tid & 15) == 0) {
-    if (a.splits == 1) {
-      if (a.lse) a.lse[bq * 16 + oh] = Lh > 0.0f ? Mh + __logf(Lh) : -INFINITY;
-    } else {
-      float* pm = a.part_ml + ((int64_t)split * a.bq_total + bq) * 32;
-      pm[2 * oh] = Mh;
-      pm[2 * oh + 1] = Lh;
+
+  // every wave holds the same (m_run, l_run) for head n
+  if (a.splits == 1) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    uint16_t* dst = a.out + (w.bq * 16 + n) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const uint2 v = make_uint2((uint32_t)f32_to_bf16_rne(acc[c][0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[c][1] * inv) << 16),
+                                 (uint32_t)f32_to_bf16_rne(acc[c][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[c][3] * inv) << 16));
+      *reinterpret_cast<uint2*>(dst + 16 * c) = v;
+    }
+    if (wave == 0 && g == 0 && a.lse) a.lse[w.bq * 16 + n] = l_run > 0.0f ? m_run + __logf(l_run) : -INFINITY;
+  } else {
+    float* po = a.part_o + ((int64_t)w.split * a.bq_total + w.bq) * 16 * 512 + n * 512 + 128 * wave + 4 * g;
+#pragma unroll
+    for (int c = 0; c < 8; c++) *reinterpret_cast<v4f*>(po + 16 * c) = acc[c];
+    if (wave == 0 && g == 0) {
+      float* pm = a.part_ml + ((int64_t)w.split * a.bq_total + w.bq) * 32;
+      pm[2 * n] = m_run;
+      pm[2 * n + 1] = l_run;
     }
   }
 }
@@ -723,10 +606,10 @@ hipError_t launch_attend(const LaunchCache& c, const int32_t* topk, uint8_t* swa
   }
   const unsigned n_wg = (unsigned)(a.splits * bq);  // (split, query) pairs in XCD-aware order
   switch (a.splits) {
-    case 10: hipLaunchKernelGGL(attend_decode_kernel, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
-    case 5: hipLaunchKernelGGL(attend_kernel<2>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attend_kernel<5>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL(attend_kernel<10>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    case 10: hipLaunchKernelGGL(attend_block_kernel<1>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(attend_block_kernel<2>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attend_block_kernel<5>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(attend_block_kernel<10>, dim3(n_wg), dim3(kThreads), 0, stream, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;

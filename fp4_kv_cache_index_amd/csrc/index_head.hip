@@ -682,7 +682,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   const uint32_t* cuts = a.ws.cut + (bq * 2 + kind) * a.ws.wstride;
   // ids of the output: entries or blocks (Full), pool slots (Reindex)
   const int64_t universe = Reindex ? (int64_t)kPool : (kind == 0 ? (int64_t)n_vis : ((int64_t)n_vis + kBlock - 1) / kBlock);
-  const bool direct = !Reindex && universe <= 32 * (int64_t)kBitWords;  // uniform: the bitmap output
+  const bool direct = universe <= 32 * (int64_t)kBitWords;  // uniform: the bitmap output
   const int nw = direct ? (int)((universe + 31) >> 5) : 0;
 
   // ---- the first R slots of every stretch (speculatively), the counts and the
@@ -798,6 +798,21 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
     hi = max(hi, L.wmx[w]);
     gfmax = max(gfmax, L.wfm[w]);
   }
+  // Reindex: the entries of this thread's candidate slots load during the
+  // selection (the same L.set positions are read at the output unless a repair
+  // changes the set)
+  constexpr int kPf = 4;
+  int32_t pe[kPf];
+  bool pf_ok = Reindex && n <= kPf * kThr;  // uniform
+  if (pf_ok) {
+    const int32_t* pool = a.pool_in + bq * kPool;
+#pragma unroll
+    for (int r = 0; r < kPf; r++) {
+      const int i = tid + r * kThr;
+      const uint64_t x = L.set[i];
+      pe[r] = pool[i < n ? key_id(x) : 0u];  // a slot below kPool
+    }
+  }
   // S* = 0 when every candidate is taken
   uint64_t s_star = n > K ? select_kth(L, n, K, lo, hi, direct) : 0ull;
   bool marked = n > K;  // the bitmap holds the selection
@@ -805,6 +820,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   // ---- while a floor is above S*, repair the share with the largest and select again
   if (gfmax > s_star) {
     marked = false;
+    pf_ok = false;
     bool query_ready = false;
     for (int round = 0; round < W; round++) {  // every round clears one share's floor
       // the share with the largest floor above S* (lowest index on ties)
@@ -920,7 +936,10 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
           pos += __popc(wd[i]);
         }
         __syncthreads();
+        // (Reindex: an id is a pool slot; the pool is ascending, so slot order
+        // is entry order, and the slot's entry is written)
         int32_t* dst = a.topk_out + bq * kTopK;
+        const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
         with_keys(L.set, n, [&](auto& b) {
 #pragma unroll
           for (int r = 0; r < b.kN; r++) {
@@ -928,7 +947,9 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
               const uint32_t id = key_id(b.x[r]);
               const uint32_t w = id >> 5;
               const int rank = (int)L.woff[w] + __popc(L.bits[w] & ((1u << (id & 31u)) - 1u));
-              if (rank < kTopK) dst[rank] = (int32_t)id;
+              int32_t v = (int32_t)id;
+              if (Reindex) v = (pf_ok && r < kPf) ? pe[r < kPf ? r : 0] : pool[id];
+              if (rank < kTopK) dst[rank] = v;
             }
           }
         });
