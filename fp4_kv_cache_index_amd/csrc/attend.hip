@@ -350,148 +350,111 @@ __device__ __forceinline__ void dequant(const Wg& w, int grp, const Raw& r, cons
 
 constexpr int kSStride = 68;  // fp32 per head row of the shared scores (64 keys + pad)
 
-// More queries, fewer splits: a workgroup takes its split's groups in blocks
-// of four (64 keys), one group per wave, as the decode kernel takes its one
-// block, with an online softmax across the blocks.  Per block every wave
-// scores its group against the query (held in registers), shares the scores
-// and its dequantised keys through LDS, takes the softmax of the block for
-// all 16 heads (so every wave holds the same running max and sum), and
-// accumulates P V for its own 128 output channels: 32 accumulator registers
-// per lane, no combine at the end.  The next block's rows load while one is
-// processed.  The query staging area and the key tile share LDS, which keeps
-// the kernel under 80 KB: two workgroups per compute unit.
-template <int kGpw>  // blocks per workgroup
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) attend_block_kernel(AttnArgs a) {
-  static_assert(16 * kQStride <= kWaves * 16 * kVStride, "the query staging fits in the key tile");
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // query staging, then keys
-  __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
-  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
-  __shared__ float s_qfac[16];
-  const Wg w = make_wg(a, kGpw);
+// One block of a split for this wave: group grp (rows in cur, id id_c) is
+// dequantised and scored against the query operand qb, the four waves' scores
+// and keys meet in LDS (s_s, s_v), and the wave folds the block's softmax into
+// its running (m_run, l_run) and P V into its 128 output channels (acc).
+// Block j > 0 first waits until every wave is past block j - 1.
+__device__ __forceinline__ void attend_block(const Wg& w, int j, int grp, const Raw& cur, int32_t id_c,
+                                             const v8h (&qb)[16], float qfac, const uint8_t* s_new, _Float16* s_v,
+                                             float* s_s, v4f (&acc)[8], float& m_run, float& l_run) {
   const int n = w.n, g = w.g, wave = w.wave;
-  // block j of this split: groups grp0 + 4j + wave
-  const int grp0 = w.split * kWaves * kGpw;
-
-  // Blocks go in pairs through a loop that is not unrolled, the rows of block
-  // j + 1 loading into the other register set while block j is processed; the
-  // loads past the last block are issued to offsets that read nothing, so no
-  // load sits under a branch.
-  int32_t id_a = load_id(w, grp0 + wave);
-  int32_t id_b = load_id(w, kGpw > 1 ? grp0 + kWaves + wave : kMainGroups);
-  uint4 qraw[4];
-  load_query(w, a, qraw);
-  float2 xv[kFusedAppendMax];
-  load_new(w, a, xv);
-  Raw ra, rb;
-  issue(w, a, grp0 + wave, id_a, ra);
-  _Float16* s_q = s_v;  // staging: [head][kQStride]
-  stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
-  lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
-  const float qfac = s_qfac[n];
-  v8h qb[16];  // the B operand of S^T = K Q^T: head n, channels 128g + 8kb .. +7
+  const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id_c)) & 0xFFFFu;  // bit k: key k exists
+  // the group's keys in two halves of each lane's 128 channels: dequantise,
+  // score and store each half into the tile (free once every wave is past
+  // the previous block), so only one half is held in registers
+  if (j > 0) lds_barrier();  // every wave is done with the previous block's tile and scores
+  v4f st = {0.f, 0.f, 0.f, 0.f};
+  _Float16* rows = s_v + wave * 16 * kVStride + n * kVStride + 128 * g;
 #pragma unroll
-  for (int kb = 0; kb < 16; kb++) qb[kb] = *reinterpret_cast<const v8h*>(s_q + n * kQStride + 128 * g + 8 * kb);
-  lds_barrier();  // every wave holds its query operand: the staging area becomes the key tile
-
-  v4f acc[8];  // O^T: acc[c][i] = O[head n][channel 128 wave + 16c + 4g + i], relative to m_run
+  for (int h = 0; h < 2; h++) {
+    uint32_t kh[32];
+    dequant(w, grp, cur, s_new, h, kh);
 #pragma unroll
-  for (int c = 0; c < 8; c++) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  // block j: its rows in cur, its id id_c; issues block j + 1's rows (id id_n)
-  // into nxt and returns block j + 2's id
-  auto block = [&](int j, Raw& cur, Raw& nxt, int32_t id_c, int32_t id_n) -> int32_t {
-    const int grp = grp0 + kWaves * j + wave;
-    const int32_t id_n2 = load_id(w, j + 2 < kGpw ? grp + 2 * kWaves : kMainGroups);
-    issue(w, a, grp + kWaves, id_n, nxt, j + 1 < kGpw);
-    const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id_c)) & 0xFFFFu;  // bit k: key k exists
-    // the group's keys in two halves of each lane's 128 channels: dequantise,
-    // score and store each half into the tile (free once every wave is past
-    // the previous block), so only one half is held in registers
-    if (j > 0) lds_barrier();  // every wave is done with the previous block's tile and scores
-    v4f st = {0.f, 0.f, 0.f, 0.f};
-    _Float16* rows = s_v + wave * 16 * kVStride + n * kVStride + 128 * g;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      uint32_t kh[32];
-      dequant(w, grp, cur, s_new, h, kh);
-#pragma unroll
-      for (int kb = 0; kb < 8; kb++) {
-        const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
-        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[8 * h + kb], st, 0, 0, 0);
-      }
-#pragma unroll
-      for (int c = 0; c < 8; c++)
-        *reinterpret_cast<uint4*>(rows + 64 * h + 8 * c) = make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
+    for (int kb = 0; kb < 8; kb++) {
+      const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
+      st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[8 * h + kb], st, 0, 0, 0);
     }
-    {
-      v4f sc;
 #pragma unroll
-      for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
-      *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
-    }
-    lds_barrier();  // every wave's scores and keys are in
+    for (int c = 0; c < 8; c++)
+      *reinterpret_cast<uint4*>(rows + 64 * h + 8 * c) = make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
+  }
+  {
+    v4f sc;
+#pragma unroll
+    for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
+    *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
+  }
+  lds_barrier();  // every wave's scores and keys are in
 
-    // ---- softmax of head n over the block: this lane holds keys 32kb + 8g .. +7
-    float sv[2][8];
+  // ---- softmax of head n over the block: this lane holds keys 32kb + 8g .. +7
+  float sv[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      const v4f lo = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g);
-      const v4f hi = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g + 4);
+  for (int kb = 0; kb < 2; kb++) {
+    const v4f lo = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g);
+    const v4f hi = *reinterpret_cast<const v4f*>(s_s + n * kSStride + 32 * kb + 8 * g + 4);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        sv[kb][i] = lo[i];
-        sv[kb][4 + i] = hi[i];
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[kb][i]);
-    mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
-    float ps = 0.0f;
-    v8h pb[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - m_new);
-        ps += pv;
-        pb[kb][i] = (_Float16)pv;
-      }
-    ps = rows_sum(ps);
-    m_run = m_new;
-    l_run = alpha * l_run + ps;
-
-    // ---- O^T = alpha O^T + V^T P^T for channels 128 wave .. +127 (alpha = 1 before the first block)
-#pragma unroll
-    for (int c = 0; c < 8; c++) acc[c] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
-#pragma unroll
-      for (int c = 0; c < 8; c++) {
-        const v4h lo = lds_read_tr16(vsrc + 16 * c);
-        const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
-        const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
-      }
-    }
-    return id_n2;
-  };
-#pragma unroll 1
-  for (int j = 0; j < kGpw; j += 2) {
-    const int32_t id_c = block(j, ra, rb, id_a, id_b);  // block j + 2's id
-    if (kGpw % 2 == 0 || j + 1 < kGpw) {  // always, for an even block count
-      const int32_t id_d = block(j + 1, rb, ra, id_b, id_c);
-      id_a = id_c;
-      id_b = id_d;
+    for (int i = 0; i < 4; i++) {
+      sv[kb][i] = lo[i];
+      sv[kb][4 + i] = hi[i];
     }
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) mx = fmaxf(mx, sv[kb][i]);
+  mx = rows_max(mx);
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
+  float ps = 0.0f;
+  v8h pb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - m_new);
+      ps += pv;
+      pb[kb][i] = (_Float16)pv;
+    }
+  ps = rows_sum(ps);
+  m_run = m_new;
+  l_run = alpha * l_run + ps;
 
+  // ---- O^T = alpha O^T + V^T P^T for channels 128 wave .. +127 (alpha = 1 before the first block)
+#pragma unroll
+  for (int c = 0; c < 8; c++) acc[c] *= alpha;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) {
+    const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const v4h lo = lds_read_tr16(vsrc + 16 * c);
+      const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
+      const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
+    }
+  }
+}
+
+// The query staged in LDS (s_q, s_qfac) and the new window tokens (s_new);
+// returns the query operand of S^T = K Q^T in qb: head n, channels 128g + 8kb .. +7.
+__device__ __forceinline__ void attend_setup(const Wg& w, const AttnArgs& a, const uint4 (&qraw)[4],
+                                             const float2 (&xv)[kFusedAppendMax], _Float16* s_q, float* s_qfac,
+                                             uint8_t* s_new, v8h (&qb)[16], float& qfac) {
+  stage_inputs(w, a, qraw, xv, s_q, s_qfac, s_new);
+  lds_barrier();  // s_q, s_qfac, s_new written; the rows stay in flight
+  qfac = s_qfac[w.n];
+#pragma unroll
+  for (int kb = 0; kb < 16; kb++) qb[kb] = *reinterpret_cast<const v8h*>(s_q + w.n * kQStride + 128 * w.g + 8 * kb);
+  lds_barrier();  // every wave holds its query operand: the staging area becomes the key tile
+}
+
+// The wave's 128 channels of the result: the bf16 output (one split) or the
+// unnormalised fp32 partial with (max, sum) per head.
+__device__ __forceinline__ void attend_finish(const Wg& w, const AttnArgs& a, const v4f (&acc)[8], float m_run,
+                                              float l_run) {
+  const int n = w.n, g = w.g, wave = w.wave;
   // every wave holds the same (m_run, l_run) for head n
   if (a.splits == 1) {
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -513,6 +476,66 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       pm[2 * n + 1] = l_run;
     }
   }
+}
+
+// More queries, fewer splits: a workgroup takes its split's groups in blocks
+// of four (64 keys), one group per wave, with an online softmax across the
+// blocks.  Per block every wave scores its group against the query (held in
+// registers), shares the scores and its dequantised keys through LDS, takes
+// the softmax of the block for all 16 heads (so every wave holds the same
+// running max and sum), and accumulates P V for its own 128 output channels:
+// 32 accumulator registers per lane, no combine at the end.  The query staging
+// area and the key tile share LDS, which keeps the kernel at 76 KB.
+//
+// attend_block_kernel: two workgroups per compute unit (244 VGPRs); the next
+// block's rows load while one is processed.  Blocks go in pairs through a loop
+// that is not unrolled; the loads past the last block are issued to offsets
+// that read nothing, so no load sits under a branch.
+template <int kGpw>  // blocks per workgroup
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) attend_block_kernel(AttnArgs a) {
+  static_assert(16 * kQStride <= kWaves * 16 * kVStride, "the query staging fits in the key tile");
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // query staging, then keys
+  __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
+  __shared__ float s_qfac[16];
+  const Wg w = make_wg(a, kGpw);
+  const int grp0 = w.split * kWaves * kGpw + w.wave;  // block j: group grp0 + 4j
+
+  int32_t id_a = load_id(w, grp0);
+  int32_t id_b = load_id(w, kGpw > 1 ? grp0 + kWaves : kMainGroups);
+  uint4 qraw[4];
+  load_query(w, a, qraw);
+  float2 xv[kFusedAppendMax];
+  load_new(w, a, xv);
+  Raw ra, rb;
+  issue(w, a, grp0, id_a, ra);
+  v8h qb[16];
+  float qfac;
+  attend_setup(w, a, qraw, xv, s_v, s_qfac, s_new, qb, qfac);
+  v4f acc[8];  // O^T: acc[c][i] = O[head n][channel 128 wave + 16c + 4g + i], relative to m_run
+#pragma unroll
+  for (int c = 0; c < 8; c++) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // block j: its rows in cur (id id_c); block j + 1's rows (id id_n) load into
+  // nxt, and block j + 2's id is returned
+  auto step = [&](int j, Raw& cur, Raw& nxt, int32_t id_c, int32_t id_n) -> int32_t {
+    const int grp = grp0 + kWaves * j;
+    const int32_t id_n2 = load_id(w, j + 2 < kGpw ? grp + 2 * kWaves : kMainGroups);
+    issue(w, a, grp + kWaves, id_n, nxt, j + 1 < kGpw);
+    attend_block(w, j, grp, cur, id_c, qb, qfac, s_new, s_v, s_s, acc, m_run, l_run);
+    return id_n2;
+  };
+#pragma unroll 1
+  for (int j = 0; j < kGpw; j += 2) {
+    const int32_t id_c = step(j, ra, rb, id_a, id_b);  // block j + 2's id
+    if (kGpw % 2 == 0 || j + 1 < kGpw) {  // always, for an even block count
+      const int32_t id_d = step(j + 1, rb, ra, id_b, id_c);
+      id_a = id_c;
+      id_b = id_d;
+    }
+  }
+  attend_finish(w, a, acc, m_run, l_run);
 }
 
 // One workgroup per (query, head): combine the splits' unnormalised partials,

@@ -512,10 +512,10 @@ def bf16_round(x):
     (1, 1, 40, 128, "decode"),        # few entries: most Top-K slots are -1, p < 127
     (2, 1, 5000, 128, "decode"),      # multi-split decode
     (3, 2, 9000, 256, "qpos"),        # explicit positions, ring larger than the window
-    (1, 100, 4000, 256, "prefill"),   # five splits: two key groups per wave
-    (1, 300, 4000, 512, "prefill"),   # two splits: five key groups per wave (rows one group ahead)
+    (1, 100, 4000, 256, "prefill"),   # five splits: two 64-key blocks per workgroup
+    (1, 300, 4000, 512, "prefill"),   # two splits: five blocks (an odd count: the last pair is half)
     (1, 520, 4000, 768, "prefill"),   # two splits
-    (1, 1100, 4000, 1280, "prefill"), # one split: ten groups per wave, no merge launch
+    (1, 1100, 4000, 1280, "prefill"), # one split: ten blocks, no merge launch
     (2, 3, 0, 128, "empty"),          # no global entries, window only
 ])
 def test_attend(csa, orc, B, Q, E, S, mode):
