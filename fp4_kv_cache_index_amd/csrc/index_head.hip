@@ -216,6 +216,21 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
 }
 
 // ------------------------------------------------------------------ head kernel
+// Batch slot `it` of workgroup j of a query: the query's W x iters batch slots
+// are dealt to its workgroups round-robin (j, j + W, ...), starting from a
+// per-query rotation so that the queries of a call read different relative
+// offsets of their sequences at any moment (Full only; Reindex has none).
+// Slots past the query's keys are skipped.
+__device__ __forceinline__ int head_rot(int64_t bq, int W, int iters, bool reindex) {
+  return reindex ? 0 : (int)(((bq & 15) * (int64_t)W * iters) >> 4);
+}
+__device__ __forceinline__ int64_t head_batch(int j, int it, int W, int iters, int rot) {
+  const int m = W * iters;
+  int x = j + it * W + rot;  // below 2m
+  if (x >= m) x -= m;
+  return x;
+}
+
 struct HeadArgs {
   const uint8_t* ik_codes;
   const float* ik_scales;
@@ -278,12 +293,14 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   }
   const int64_t row_base = (int64_t)b * a.cap;
   const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
+  const int rot = head_rot(bq, W, a.iters, Reindex);
 
   // ---- fused append: the new entries in this workgroup's batches, one wave each
   if (!Reindex && fits) {
     for (int t = wave; t < a.app_T; t += kScoreWaves) {  // wave-uniform
       const int64_t e = (int64_t)len0 + t;
-      if ((e / kBatchKeys) % W != j || q != 0) continue;  // the first query's workgroup of that batch writes it
+      const int owner = (int)((((e / kBatchKeys) - rot) % W + W) % W);  // the workgroup holding e's batch slot
+      if (owner != j || q != 0) continue;  // the first query's workgroup of that batch writes it
       const float4* src = reinterpret_cast<const float4*>(a.app_kv + ((int64_t)b * a.app_T + t) * 512 + 8 * lane);
       const float4 v0 = src[0], v1 = src[1];
       const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -307,7 +324,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
 #pragma unroll
     for (int it = 0; it < kIters; it++)
 #pragma unroll
-      for (int jj = 0; jj < kBatch; jj++) pe[it][jj] = pool[(int64_t)(j + it * W) * kBatchKeys + sc.key_of(jj)];
+      for (int jj = 0; jj < kBatch; jj++) pe[it][jj] = pool[head_batch(j, it, W, a.iters, rot) * kBatchKeys + sc.key_of(jj)];
     if (kDebug)
       for (int it = 0; it < kIters; it++)
         for (int jj = 0; jj < kBatch; jj++)
@@ -319,7 +336,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
       for (int jj = 0; jj < kBatch; jj++) pe[it][jj] = 0;
   }
   const int64_t n_keys = Reindex ? (int64_t)kPool : (int64_t)n_vis;  // keys of the query
-  auto base_of = [&](int it) -> int64_t { return (int64_t)(j + it * W) * kBatchKeys; };
+  auto base_of = [&](int it) -> int64_t { return head_batch(j, it, W, a.iters, rot) * kBatchKeys; };
   auto live = [&](int it) -> bool { return it < a.iters && base_of(it) < n_keys; };  // uniform
   BatchLoad ld[2];
   if (live(0)) sc.issue(base_of(0), pe[0], ld[0]);
@@ -340,7 +357,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   for (int it = 0; it < kIters; it++) {
     ks[0][it] = 0u;
     ks[1][it] = 0u;
-    if (!live(it)) continue;  // uniform; the later batches are past the keys too
+    if (!live(it)) continue;  // uniform
     if (it >= 1 && it + 1 < kIters && live(it + 1)) sc.issue(base_of(it + 1), pe[it + 1], ld[(it + 1) & 1]);
     const int64_t k_own = base_of(it) + sc.own();
     bool valid;
@@ -633,9 +650,10 @@ __device__ __forceinline__ void repair_share(const SelectArgs& a, int64_t bq, in
   sc.load_query(L.q8, L.c);
   const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
   const int64_t n_keys = Reindex ? (int64_t)kPool : (int64_t)n_vis;
+  const int rot = head_rot(bq, W, a.iters, Reindex);
   for (int it = 0; it < a.iters; it++) {
-    const int64_t base = (int64_t)(j + it * W) * kBatchKeys;
-    if (base >= n_keys) break;  // uniform
+    const int64_t base = head_batch(j, it, W, a.iters, rot) * kBatchKeys;
+    if (base >= n_keys) continue;  // uniform
     int32_t pe[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; jj++) pe[jj] = Reindex ? pool[base + sc.key_of(jj)] : 0;
