@@ -357,8 +357,10 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   for (int it = 0; it < kIters; it++) {
     ks[0][it] = 0u;
     ks[1][it] = 0u;
-    if (!live(it)) continue;  // uniform
+    // the next live batch's loads, issued before this batch's liveness is known:
+    // with the rotation a dead slot can sit between two live ones
     if (it >= 1 && it + 1 < kIters && live(it + 1)) sc.issue(base_of(it + 1), pe[it + 1], ld[(it + 1) & 1]);
+    if (!live(it)) continue;  // uniform
     const int64_t k_own = base_of(it) + sc.own();
     bool valid;
     if constexpr (Reindex) {

@@ -225,6 +225,25 @@ def test_index_full_topk_and_pool(csa, orc, E):
     print(f"E={E}: boundary swaps {swaps}")
 
 
+def test_index_full_ragged_batch_slots(csa, orc):
+    """Sixteen sequences of very different lengths in one capacity: each query's
+    batches are dealt over its workgroups' slots from its own rotation, so dead
+    slots (past the query's keys) sit between live ones, and a workgroup must
+    still have its next live batch in flight."""
+    B, cap = 16, 40000
+    lengths = [cap - 2500 * b for b in range(B)]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 23)
+    iq = synth.normal(23, "iq_ragged_slots", (B, 1, 4, 64))
+    ref_topk, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq)
+    swaps = 0
+    for b in range(B):
+        swaps += topk_swaps(topk[b, 0], ref_topk[b, 0], scores[b, 0], name=f"topk b{b}")
+        swaps += pool_block_swaps(pool[b, 0], ref_pool[b, 0], scores[b, 0], lengths[b], name=f"pool b{b}")
+    print(f"ragged batch slots: boundary swaps {swaps}")
+
+
 @pytest.mark.parametrize("Q", [1, 6])  # the one-query scorer / the eight-query scorer
 def test_index_empty_sequences(csa, orc, Q):
     """Sequences with no entry, and queries placed before the first entry, get
