@@ -124,6 +124,7 @@ struct HeadLds {
   uint32_t wmax[2][kScoreWaves];    // largest key of each wave, per kind
   uint32_t cut[2];
   int n[2];                         // keys written, per kind (zero before write_heads)
+  uint32_t wlive[2][kScoreWaves];   // each wave's nonzero keys, per kind
   uint64_t wfloor[2][kScoreWaves];  // largest key each wave does not write, per kind
 };
 
@@ -160,13 +161,16 @@ __device__ uint32_t head_cut(const uint32_t* hist, uint32_t mx, int T, int T_cap
 // [j T_cap, j T_cap + count) of each kind), with the count, the cut and the
 // floor: the largest key it did not write.  ks[kind][it]: this lane's key of
 // batch it (0 = none; a block key is held by lane 8b of its block only);
-// idf(kind, it): the key's id.  H.wmax holds every wave's largest key and H.n
-// is zero (the caller has synchronised after the histograms).  T: keys wanted,
-// T_cap: most keys a share may write.  Out-pointers are kind 0's; kind 1's
-// follow at `stride`.
+// idf(kind, it): the key's id.  H.wmax and H.wlive hold every wave's largest
+// key and count of keys, and H.n is zero (the caller has synchronised after the
+// histograms).  The share wants T = 1.5 K live / total + 16 keys of a kind: one
+// and a half times its share of the K selected, in proportion to its keys
+// among the query's `total` (a Reindex pool shorter than its slots leaves most
+// shares empty); T_cap: most keys a share may write.  Out-pointers are kind
+// 0's; kind 1's follow at `stride`.
 template <int kIters, typename IdF>
 __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf, const uint32_t* hist0,
-                            const uint32_t* hist1, const int32_t (&T)[2], const int32_t (&T_cap)[2], int j,
+                            const uint32_t* hist1, const int64_t (&total)[2], const int32_t (&T_cap)[2], int j,
                             uint64_t* cand, uint32_t* count_out, uint64_t* floor_out, uint32_t* cut_out,
                             int32_t stride, HeadLds& H) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -174,10 +178,16 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
   for (int kind = 0; kind < 2; kind++) {
     if (kind >= kinds) break;  // uniform
     // every wave finds the same cut
-    uint32_t mx = 0u;
+    uint32_t mx = 0u, live = 0u;
 #pragma unroll
-    for (int w = 0; w < kScoreWaves; w++) mx = max(mx, H.wmax[kind][w]);
-    const uint32_t cut = head_cut(kind ? hist1 : hist0, mx, T[kind], T_cap[kind]);
+    for (int w = 0; w < kScoreWaves; w++) {
+      mx = max(mx, H.wmax[kind][w]);
+      live += H.wlive[kind][w];
+    }
+    const int64_t K = kind ? kPoolBlocks : kTopK;
+    const int64_t want = total[kind] > 0 ? (3 * K * live + 2 * total[kind] - 1) / (2 * total[kind]) + 16 : 0;
+    const int T = (int)min(want, (int64_t)T_cap[kind]);
+    const uint32_t cut = head_cut(kind ? hist1 : hist0, mx, T, T_cap[kind]);
     // this lane's written keys and the largest unwritten one
     uint32_t mine = 0u;
     uint64_t fl = 0ull;
@@ -248,7 +258,7 @@ struct HeadArgs {
   int32_t W;          // workgroups per query
   int32_t iters;      // batches per workgroup (at most kFullIters / kReindexIters)
   int32_t blocks;     // Full: also the pool's block keys
-  int32_t T[2], T_cap[2];
+  int32_t T[2], T_cap[2];  // keys a share wants with evenly spread keys (the select's speculative loads); most it writes
   const float* app_kv;  // fused append: [B][app_T][512] f32 new entries (ratio 1), or null
   const float* app_ik;  // [B][app_T][64] f32
   int32_t app_T;
@@ -380,11 +390,21 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
     }
   }
   kmax = wave_max(kmax);  // the block keys' maximum is the same key
+  uint32_t live0 = 0u, live1 = 0u;
+#pragma unroll
+  for (int it = 0; it < kIters; it++) {
+    live0 += ks[0][it] != 0u ? 1u : 0u;
+    live1 += ks[1][it] != 0u ? 1u : 0u;
+  }
+  live0 = wave_sum(live0);
+  live1 = wave_sum(live1);
   if (lane == 0) {
     H.wmax[0][wave] = kmax;
     H.wmax[1][wave] = kmax;
+    H.wlive[0][wave] = live0;
+    H.wlive[1][wave] = live1;
   }
-  __syncthreads();  // the histograms and maxima are complete
+  __syncthreads();  // the histograms, maxima and counts are complete
 
   const int64_t sl = (bq * 2) * a.ws.wstride + j;  // this share's floor and cut, kind 0
   auto idf = [&](int kind, int it) -> uint32_t {  // entry or pool slot; block
@@ -392,7 +412,12 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
     return (uint32_t)(kind ? (k >> 3) : k);
   };
   const int kinds = (!Reindex && a.blocks) ? 2 : 1;
-  write_heads<kIters>(ks, kinds, idf, s_hist, s_bhist, a.T, a.T_cap, j, a.ws.cand + (bq * 2) * kHeadCap,
+  // keys of each kind over all the query's shares: its visible entries and their
+  // blocks, or the entries of its pool (every visible one while they are fewer
+  // than the pool's slots)
+  const int64_t total[2] = {Reindex ? min((int64_t)n_vis, (int64_t)kPool) : (int64_t)n_vis,
+                            ((int64_t)n_vis + kBlock - 1) / kBlock};
+  write_heads<kIters>(ks, kinds, idf, s_hist, s_bhist, total, a.T_cap, j, a.ws.cand + (bq * 2) * kHeadCap,
                       a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.wstride, H);
 }
 
@@ -1130,9 +1155,11 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
 // ------------------------------------------------------------------ launch
 CSA2_DEV_ERROR_TAKER(take_head_dev_error)
 
-// per share: the keys wanted (one and a half times its even share of K, plus
-// 16) and the most it may write (the query's kHeadCap split evenly).  A share
-// holding more of the Top-K than it wrote is re-scored by the select kernel.
+// per share: the keys wanted when every share holds as many keys (one and a
+// half times its even share of K, plus 16; each share scales this by its own
+// keys in the kernel) and the most it may write (the query's kHeadCap split
+// evenly).  A share holding more of the Top-K than it wrote is re-scored by
+// the select kernel.
 static void head_targets(int W, int K, int32_t& T, int32_t& T_cap) {
   T_cap = (kHeadCap / W) & ~1;  // even: the select kernel loads slot pairs
   const int want = (3 * K + 2 * W - 1) / (2 * W) + 16;
