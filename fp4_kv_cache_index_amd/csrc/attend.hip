@@ -189,7 +189,7 @@ __device__ __forceinline__ Wg make_wg(const AttnArgs& a, int gpw) {
   w.b = (int)(w.bq / a.Q);
   w.qi = (int)(w.bq % a.Q);
   w.tid = threadIdx.x;
-  w.wave = w.tid >> 6;
+  w.wave = __builtin_amdgcn_readfirstlane(w.tid >> 6);  // uniform in the wave: the buffer descriptors it selects stay scalar
   w.n = w.tid & 15;
   w.g = (w.tid & 63) >> 4;
   w.p = a.q_pos ? a.q_pos[w.bq] : a.length[w.b] * a.ratio - a.Q + w.qi;
