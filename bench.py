@@ -621,7 +621,7 @@ def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
     if head:
         parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false>", True))
     else:
-        parts = (("score", "index_score_kernel<4096, false>", False), ("filter", "index_filter_kernel", False),
+        parts = (("score", "index_scoreq_kernel<", False), ("filter", "index_filter_kernel", False),
                  ("final", "index_final_kernel", True))
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):

@@ -58,15 +58,15 @@ def test_counter_summary(tmp_path, monkeypatch):
 
     copy = "__amd_rocclr_copyBuffer"
     fetch = [(copy, 4096, 999.0),  # an earlier copy: not a calibration copy
-             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 70000.0),
-             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 70002.0),
+             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 70000.0),
+             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 70002.0),
              ("csa2::index_filter_kernel(...)", 131072, 5000.0),
              ("csa2::index_final_kernel(...)", 16384, 600.0),     # the Full call's (kinds x queries)
              ("csa2::index_final_kernel(...)", 8192, 12345.0),    # a Reindex call's: left out
-             ("void csa2::index_score_kernel<1024, true>(...)", 131072, 777.0),
+             ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 777.0),
              (copy, 65536, 131072.0), (copy, 65536, 131072.0), (copy, 65536, 131072.0)]
     write = [(copy, 4096, 999.0),
-             ("void csa2::index_score_kernel<4096, false>(...)", 270336, 9500.0),
+             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 9500.0),
              ("csa2::index_filter_kernel(...)", 131072, 600.0),
              ("csa2::index_final_kernel(...)", 16384, 1600.0),
              ("csa2::index_final_kernel(...)", 8192, 54321.0),
