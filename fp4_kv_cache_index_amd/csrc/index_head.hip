@@ -3,8 +3,10 @@
 // technologiesdigest "CSA2" for the modes and Top-512; ai.info "Methodology in
 // Plain English" for the hierarchical pool: the first Full layer keeps the
 // 2,048 aligned 8-entry blocks whose largest index score ranks highest).
-// Used for one to three queries per sequence; more queries go through the
-// shared-load scorer in index.hip.
+// Used for one to three queries per sequence and for Reindex; four or more
+// queries of a sequence without a pool (prefill chunks) share each key load in
+// index_shared_head, which writes heads of the same form; four or more with a
+// pool go through the shared-load scorer in index.hip.
 //
 // Two kernels per call.
 //  1. index_head: W workgroups per query each score one share of the keys
@@ -80,9 +82,19 @@ int head_workgroups(bool reindex, int32_t capacity, int64_t bq) {
   return (int)(w > 0 ? w : 1);
 }
 
+// Workgroups per query of the shared-load heads (four or more queries per
+// sequence, no pool): every share holds at most kSharedIters batches.
+constexpr int kSharedIters = 8;
+int shared_head_workgroups(int32_t capacity) {
+  const int64_t batches = ((int64_t)capacity + kBatchKeys - 1) / kBatchKeys;
+  const int64_t w = (batches + kSharedIters - 1) / kSharedIters;
+  return (int)(w > 0 ? w : 1);
+}
+
 static inline int head_wmax(int32_t capacity, int64_t bq) {
   const int a = head_workgroups(false, capacity, bq), b = head_workgroups(true, capacity, bq);
-  return a > b ? a : b;
+  const int c = shared_head_workgroups(capacity);
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
 size_t head_ws_bytes(int64_t bq, int32_t capacity) {
@@ -134,13 +146,14 @@ struct HeadLds {
 // the keys above it and in it fit in T_cap; otherwise only the keys above it,
 // fewer than T, are written).  With fewer than T keys in all, every key is
 // written (cut = 0 << 1 | 1).
-__device__ uint32_t head_cut(const uint32_t* hist, uint32_t mx, int T, int T_cap) {
+template <typename CountF>
+__device__ uint32_t head_cut(CountF count_of, uint32_t mx, int T, int T_cap) {
   const int lane = threadIdx.x & 63;
   int b_hi = mx ? (int)(mx >> kBinShift) : -1;
   uint32_t above = 0u;
   while (b_hi >= 0) {
     const int bn = b_hi - lane;
-    const uint32_t cnt = bn >= 0 ? hist[bn] : 0u;
+    const uint32_t cnt = bn >= 0 ? count_of(bn) : 0u;
     const uint32_t incl = wave_incl_scan(cnt);
     const uint32_t tot = readlane(incl, 63);
     if (above + tot >= (uint32_t)T) {
@@ -187,7 +200,8 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     const int64_t K = kind ? kPoolBlocks : kTopK;
     const int64_t want = total[kind] > 0 ? (3 * K * live + 2 * total[kind] - 1) / (2 * total[kind]) + 16 : 0;
     const int T = (int)min(want, (int64_t)T_cap[kind]);
-    const uint32_t cut = head_cut(kind ? hist1 : hist0, mx, T, T_cap[kind]);
+    const uint32_t* hist = kind ? hist1 : hist0;
+    const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
     // this lane's written keys and the largest unwritten one
     uint32_t mine = 0u;
     uint64_t fl = 0ull;
@@ -421,6 +435,252 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
                       a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.wstride, H);
 }
 
+// ------------------------------------------------------------------ shared-load heads
+// Four or more queries per sequence and no pool (prefill chunks, multi-token
+// decode without a pool): 4G queries of one sequence share every key load, and
+// each query's keys stay in registers, as at one query.  Workgroup (group, j)
+// scores batches j, j + W, ... (no rotation: the group's queries share them),
+// counts every query's keys in its own LDS histogram (two 16-bit counts per
+// word: a share holds at most 4,096 keys), and writes each query's heads,
+// count, floor and cut to that query's stretch j as index_head does.  The
+// select kernel then completes the call unchanged: its repair re-scores a
+// share with the one-query scoring core, whose keys are bit for bit these
+// (the same two MFMAs per 16 keys, head sum and scale, in the same order).
+struct SharedHeadArgs {
+  const uint8_t* ik_codes;
+  const float* ik_scales;
+  const int32_t* length;
+  int32_t cap, ratio;
+  const float* iq;
+  const float* iw;
+  const int32_t* q_pos;
+  int32_t Q, W, iters, T_cap;
+  HeadWs ws;
+};
+
+template <int G>
+__global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(SharedHeadArgs a) {
+  constexpr int kQ = 4 * G;                 // queries per workgroup
+  constexpr int kJ = kScoreThreads / 256;  // queries whose elements one pass of the workgroup loads
+  static_assert(kQ % kJ == 0 && kQ <= kScoreWaves, "whole passes; one wave per query's cut");
+  __shared__ uint32_t s_hist[kQ][kBins / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q8[kQ][256];
+  __shared__ float s_c[kQ][4];
+  __shared__ uint32_t s_max[kQ], s_live[kQ], s_cut[kQ];
+  __shared__ uint32_t s_n[kQ];
+  __shared__ unsigned long long s_floor[kQ];
+
+  const int j = blockIdx.y, W = a.W, Q = a.Q;
+  const int groups_per_seq = (Q + kQ - 1) / kQ;
+  const int b = (int)(blockIdx.x / groups_per_seq), q0 = (int)(blockIdx.x % groups_per_seq) * kQ;
+  const int nq = min(kQ, Q - q0);
+  const int64_t bq0 = (int64_t)b * Q + q0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15, grp = lane >> 4, jq = lane >> 4;
+  // query elements first (thread 256 jh + t quantises element t of queries
+  // jh, jh + kJ, ...; a missing query reloads the last one, unused)
+  const int t = tid & 255, jh = tid >> 8;
+  float iq_v[kQ / kJ], iw_v[kQ / kJ];
+#pragma unroll
+  for (int k = 0; k < kQ / kJ; k++) {
+    const int64_t jj = bq0 + min(jh + kJ * k, nq - 1);
+    iq_v[k] = a.iq[jj * 256 + t];
+    iw_v[k] = a.iw ? a.iw[jj * 4 + (t >> 6)] : 1.0f;
+  }
+  const int32_t len = a.length[b];
+  if (kDebug && j == 0 && q0 == 0 && tid == 0 && (len < 0 || len > a.cap)) dev_flag(kErrLength);
+  int32_t nv[kQ];
+  int32_t nv_max = 0;
+#pragma unroll
+  for (int u = 0; u < kQ; u++) {
+    nv[u] = u < nq ? visible_count(len, a.cap, a.ratio, query_pos(a.q_pos, a.length, a.ratio, b, q0 + u, Q)) : 0;
+    nv_max = max(nv_max, nv[u]);
+  }
+  nv_max = __builtin_amdgcn_readfirstlane(nv_max);
+  if (j == 0 && tid < nq) {
+    int32_t v = 0;
+#pragma unroll
+    for (int u = 0; u < kQ; u++) v = u == tid ? nv[u] : v;
+    a.ws.nvis[(bq0 + tid) * 2] = v;
+    a.ws.nvis[(bq0 + tid) * 2 + 1] = -1;  // no length to store
+  }
+
+  const int64_t row_base = (int64_t)b * a.cap;
+  const BufRsrc kr = make_rsrc(a.ik_codes + row_base * 64, (uint32_t)nv_max * 64u);
+  const BufRsrc sr = make_rsrc(a.ik_scales + row_base, (uint32_t)nv_max * 4u);
+  auto base_of = [&](int it) -> int64_t { return head_batch(j, it, W, a.iters, 0) * kBatchKeys; };
+  // batches ascend with it, so the live ones come first
+  auto live = [&](int it) -> bool { return it < a.iters && base_of(it) < nv_max; };  // uniform
+  auto issue = [&](int it, v4i (&bytes)[kBatch], float (&sk)[kBatch]) {
+    const int64_t base = base_of(it);
+#pragma unroll
+    for (int jj = 0; jj < kBatch; jj++) {
+      const uint32_t e = (uint32_t)(base + 16 * (jj * kScoreWaves + wave) + row);
+      bytes[jj] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kr, e * 64u + 16u * grp, 0, kNT));
+      sk[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, e * 4u, 0, 0));
+    }
+  };
+  v4i bytes[2][kBatch];
+  float sk[2][kBatch];
+  if (live(0)) issue(0, bytes[0], sk[0]);
+  if (live(1)) issue(1, bytes[1], sk[1]);
+
+  for (int i = tid; i < kQ * kBins / 2; i += kScoreThreads) (&s_hist[0][0])[i] = 0u;
+  if (tid < kQ) {
+    s_max[tid] = 0u;
+    s_live[tid] = 0u;
+    s_n[tid] = 0u;
+    s_floor[tid] = 0ull;
+  }
+#pragma unroll
+  for (int k = 0; k < kQ / kJ; k++) {
+    const int jx = jh + kJ * k;
+    if (jx < nq) {
+      prep_query(iq_v[k], iw_v[k], s_q8[jx], s_c[jx], t);
+    } else {
+      s_q8[jx][t] = 0;
+      if (t < 4) s_c[jx][t] = 0.0f;
+    }
+  }
+  lds_barrier();  // LDS only: the first batches stay in flight
+
+  // A operands: in group g, row r = lane%16 is query 4g + r/4, head r%4;
+  // lanes 16jq..16jq+15 finish query 4g + jq's keys
+  v8bf qa0[G], qa1[G];
+  float ch[G][4];
+  int32_t my_nv[G];
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&s_q8[4 * g + (row >> 2)][(row & 3) * 64 + 16 * grp]);
+    qa0[g] = widen8(src[0], src[1]);
+    qa1[g] = widen8(src[2], src[3]);
+    const int jx = 4 * g + jq;
+#pragma unroll
+    for (int h = 0; h < 4; h++) ch[g][h] = s_c[jx][h];
+    int32_t v = 0;
+#pragma unroll
+    for (int u = 0; u < kQ; u++) v = u == jx ? nv[u] : v;
+    my_nv[g] = jx < nq ? v : 0;  // a missing query has no keys
+  }
+
+  uint32_t ks[kSharedIters][kBatch][G];  // this lane's keys: batch, group, query 4g + jq
+  uint32_t kmax[G], nlive[G];
+#pragma unroll
+  for (int g = 0; g < G; g++) kmax[g] = nlive[g] = 0u;
+#pragma unroll
+  for (int it = 0; it < kSharedIters; it++) {
+#pragma unroll
+    for (int jj = 0; jj < kBatch; jj++)
+#pragma unroll
+      for (int g = 0; g < G; g++) ks[it][jj][g] = 0u;
+    if (it >= 1 && it + 1 < kSharedIters && live(it + 1)) issue(it + 1, bytes[(it + 1) & 1], sk[(it + 1) & 1]);
+    if (!live(it)) continue;  // uniform
+    const int64_t base = base_of(it);
+    const v4i(&by)[kBatch] = bytes[it & 1];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; jj++) {
+      const v8bf k0 = widen8((uint32_t)by[jj][0], (uint32_t)by[jj][1]);
+      const v8bf k1 = widen8((uint32_t)by[jj][2], (uint32_t)by[jj][3]);
+      const int64_t e = base + 16 * (jj * kScoreWaves + wave) + row;
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0[g], k0, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1[g], k1, d, 0, 0, 0);
+        float acc = 0.0f;
+        acc = __builtin_fmaf(ch[g][0], d[0] > 0.0f ? d[0] : 0.0f, acc);
+        acc = __builtin_fmaf(ch[g][1], d[1] > 0.0f ? d[1] : 0.0f, acc);
+        acc = __builtin_fmaf(ch[g][2], d[2] > 0.0f ? d[2] : 0.0f, acc);
+        acc = __builtin_fmaf(ch[g][3], d[3] > 0.0f ? d[3] : 0.0f, acc);
+        const uint32_t key = e < my_nv[g] ? order_key(sk[it & 1][jj] * acc) : 0u;
+        ks[it][jj][g] = key;
+        kmax[g] = max(kmax[g], key);
+        nlive[g] += key != 0u ? 1u : 0u;
+        const uint32_t bin = key >> kBinShift;
+        if (key) atomicAdd(&s_hist[4 * g + jq][bin >> 1], 1u << (16 * (bin & 1u)));
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    if (4 * g + jq < nq) {
+      atomicMax(&s_max[4 * g + jq], kmax[g]);
+      atomicAdd(&s_live[4 * g + jq], nlive[g]);
+    }
+  }
+  __syncthreads();  // the histograms, maxima and counts are complete
+
+  // wave u finds query u's cut: the bin holding the share's T-th key, with T in
+  // proportion to the share's keys among the query's visible entries
+  if (wave < nq) {  // uniform
+    int32_t total = 0;
+#pragma unroll
+    for (int u = 0; u < kQ; u++) total = u == wave ? nv[u] : total;
+    const uint32_t lv = s_live[wave];
+    const int64_t want = total > 0 ? (3 * (int64_t)kTopK * lv + 2 * (int64_t)total - 1) / (2 * (int64_t)total) + 16 : 0;
+    const int T = (int)min(want, (int64_t)a.T_cap);
+    const uint32_t* h = s_hist[wave];
+    const uint32_t cut = head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
+    if (lane == 0) s_cut[wave] = cut;
+  }
+  __syncthreads();
+
+  // each query's keys above its cut to its stretch j; the largest other key is
+  // its floor.  A key x is written iff x >= thr (head_written as one compare:
+  // thr is the cut bin's lowest key when that bin is written, else the next
+  // bin's, and at least 1); ids ascend with (it, jj) in a lane, so the first
+  // unwritten key of the largest value has the lowest id.
+  uint32_t loff[kBatch];
+#pragma unroll
+  for (int jj = 0; jj < kBatch; jj++) loff[jj] = (uint32_t)(16 * (jj * kScoreWaves + wave) + row);
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    const int jx = 4 * g + jq;
+    if (jx >= nq) continue;
+    const uint32_t cut = s_cut[jx];
+    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
+    const bool any = thr64 <= 0xFFFFFFFFull;  // not past the top bin
+    const uint32_t thr = thr64 > 1ull ? (uint32_t)thr64 : 1u;
+    uint32_t mine = 0u, fx = 0u, fid = 0u;
+#pragma unroll
+    for (int it = 0; it < kSharedIters; it++) {
+      const uint32_t sb = (uint32_t)base_of(it);
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        const uint32_t x = ks[it][jj][g];
+        const bool w = any && x >= thr;
+        mine += w ? 1u : 0u;
+        const uint32_t xu = w ? 0u : x;
+        const bool up = xu > fx;
+        fx = up ? xu : fx;
+        fid = up ? sb + loff[jj] : fid;
+      }
+    }
+    uint32_t slot = atomicAdd(&s_n[jx], mine);
+    uint64_t* dst = a.ws.cand + ((bq0 + jx) * 2) * kHeadCap + (int64_t)j * a.T_cap;
+#pragma unroll
+    for (int it = 0; it < kSharedIters; it++) {
+      const uint32_t sb = (uint32_t)base_of(it);
+#pragma unroll
+      for (int jj = 0; jj < kBatch; jj++) {
+        const uint32_t x = ks[it][jj][g];
+        if (any && x >= thr) {
+          if (slot < (uint32_t)a.T_cap) dst[slot] = key64(x, sb + loff[jj]);  // the cap always holds
+          slot++;
+        }
+      }
+    }
+    if (fx) atomicMax(&s_floor[jx], (unsigned long long)key64(fx, fid));
+  }
+  __syncthreads();
+  if (tid < nq) {
+    const int64_t sl = ((bq0 + tid) * 2) * a.ws.wstride + j;
+    a.ws.floor[sl] = s_floor[tid];
+    a.ws.cut[sl] = s_cut[tid];
+    a.ws.count[sl] = min(s_n[tid], (uint32_t)a.T_cap);
+  }
+}
+
 // ------------------------------------------------------------------ select kernel
 struct SelectArgs {
   const uint8_t* ik_codes;
@@ -431,6 +691,7 @@ struct SelectArgs {
   const float* iw;
   const int32_t* pool_in;
   int32_t Q, W, iters, app_T;
+  int32_t rotate;  // the head kernel's per-query batch rotation (0: the shared-load heads, none)
   int32_t tc;  // each workgroup's stretch of the candidate list (even, W tc <= kHeadCap)
   // per kind: the slots of each stretch loaded before the counts are known (R,
   // even, <= tc) and floor(2^32 / (R / 2)) + 1, so that p / (R / 2) ==
@@ -677,7 +938,7 @@ __device__ __forceinline__ void repair_share(const SelectArgs& a, int64_t bq, in
   sc.load_query(L.q8, L.c);
   const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
   const int64_t n_keys = Reindex ? (int64_t)kPool : (int64_t)n_vis;
-  const int rot = head_rot(bq, W, a.iters, Reindex);
+  const int rot = a.rotate ? head_rot(bq, W, a.iters, Reindex) : 0;
   for (int it = 0; it < a.iters; it++) {
     const int64_t base = head_batch(j, it, W, a.iters, rot) * kBatchKeys;
     if (base >= n_keys) continue;  // uniform
@@ -1166,6 +1427,47 @@ static void head_targets(int W, int K, int32_t& T, int32_t& T_cap) {
   T = want < T_cap ? want : T_cap;
 }
 
+// The select kernel over the heads of W shares per query (iters batches each).
+static hipError_t launch_select(const LaunchCache& c, bool reindex, const float* iq, const float* iw,
+                                const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, int W,
+                                int iters, int32_t app_T, int rotate, int kinds, const HeadWs& ws,
+                                hipStream_t stream) {
+  const int64_t bq = (int64_t)c.batch * Q;
+  int32_t T[2], T_cap[2];
+  head_targets(W, kTopK, T[0], T_cap[0]);
+  head_targets(W, kPoolBlocks, T[1], T_cap[1]);
+  SelectArgs s;
+  s.ik_codes = c.ik_codes;
+  s.ik_scales = c.ik_scales;
+  s.length = c.length;
+  s.cap = c.capacity;
+  s.ratio = c.ratio;
+  s.iq = iq;
+  s.iw = iw;
+  s.pool_in = pool_in;
+  s.Q = Q;
+  s.W = W;
+  s.iters = iters;
+  s.app_T = app_T;
+  s.rotate = rotate;
+  s.tc = T_cap[0];
+  for (int k = 0; k < 2; k++) {
+    // twice the keys wanted covers a share's count but for a wide boundary bin
+    const int r = 2 * T[k] < s.tc ? 2 * T[k] : s.tc;
+    s.spec[k] = (r + 1) & ~1;
+    s.spec_magic[k] = (uint32_t)((1ull << 32) / (uint64_t)(s.spec[k] / 2) + 1ull);
+  }
+  s.ws = ws;
+  s.topk_out = topk_out;
+  s.pool_out = reindex ? nullptr : pool_out;
+  const dim3 sgrid((unsigned)bq, (unsigned)kinds);
+  if (reindex)
+    hipLaunchKernelGGL(index_select_kernel<true>, sgrid, dim3(kScoreThreads), 0, stream, s);
+  else
+    hipLaunchKernelGGL(index_select_kernel<false>, sgrid, dim3(kScoreThreads), 0, stream, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq, const float* iw,
                              const int32_t* q_pos, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
                              int32_t Q, const float* app_kv, const float* app_ik, int32_t app_T, void* ws_head,
@@ -1209,35 +1511,41 @@ hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq
     hipLaunchKernelGGL(index_head_kernel<false>, grid, dim3(kScoreThreads), 0, stream, h);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SelectArgs s;
-  s.ik_codes = c.ik_codes;
-  s.ik_scales = c.ik_scales;
-  s.length = c.length;
-  s.cap = c.capacity;
-  s.ratio = c.ratio;
-  s.iq = iq;
-  s.iw = iw;
-  s.pool_in = pool_in;
-  s.Q = Q;
-  s.W = h.W;
-  s.iters = h.iters;
-  s.app_T = app_T;
-  s.tc = h.T_cap[0];
-  for (int k = 0; k < 2; k++) {
-    // twice the keys wanted covers a share's count but for a wide boundary bin
-    const int r = 2 * h.T[k] < s.tc ? 2 * h.T[k] : s.tc;
-    s.spec[k] = (r + 1) & ~1;
-    s.spec_magic[k] = (uint32_t)((1ull << 32) / (uint64_t)(s.spec[k] / 2) + 1ull);
-  }
-  s.ws = h.ws;
-  s.topk_out = topk_out;
-  s.pool_out = reindex ? nullptr : pool_out;
-  const dim3 sgrid((unsigned)bq, (unsigned)kinds);
-  if (reindex)
-    hipLaunchKernelGGL(index_select_kernel<true>, sgrid, dim3(kScoreThreads), 0, stream, s);
-  else
-    hipLaunchKernelGGL(index_select_kernel<false>, sgrid, dim3(kScoreThreads), 0, stream, s);
-  return hipGetLastError();
+  return launch_select(c, reindex, iq, iw, pool_in, topk_out, pool_out, Q, h.W, h.iters, app_T, 1, kinds, h.ws,
+                       stream);
+}
+
+// Full with four or more queries per sequence and no pool: the shared-load
+// heads, four queries per workgroup, then the select kernel.  (Eight per
+// workgroup share each load twice as widely, but their 64 keys per lane leave
+// room for one workgroup per compute unit, not two: slower at the
+// 2,048-query prefill.)
+hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, const float* iw, const int32_t* q_pos,
+                                     int32_t* topk_out, int32_t Q, void* ws_head, hipStream_t stream) {
+  const int64_t bq = (int64_t)c.batch * Q;
+  if (bq == 0) return hipSuccess;
+  const int qpw = 4;
+  SharedHeadArgs h;
+  h.ik_codes = c.ik_codes;
+  h.ik_scales = c.ik_scales;
+  h.length = c.length;
+  h.cap = c.capacity;
+  h.ratio = c.ratio;
+  h.iq = iq;
+  h.iw = iw;
+  h.q_pos = q_pos;
+  h.Q = Q;
+  h.W = shared_head_workgroups(c.capacity);
+  const int64_t batches = ((int64_t)c.capacity + kBatchKeys - 1) / kBatchKeys;
+  h.iters = (int32_t)((batches + h.W - 1) / h.W);  // at most kSharedIters
+  int32_t T;
+  head_targets(h.W, kTopK, T, h.T_cap);
+  h.ws = head_ws_carve(ws_head, bq, c.capacity);
+  const dim3 grid((unsigned)(c.batch * ((Q + qpw - 1) / qpw)), (unsigned)h.W);
+  hipLaunchKernelGGL(index_shared_head_kernel<1>, grid, dim3(kScoreThreads), 0, stream, h);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select(c, false, iq, iw, nullptr, topk_out, nullptr, Q, h.W, h.iters, 0, 0, 1, h.ws, stream);
 }
 
 }  // namespace csa2

@@ -45,7 +45,8 @@ struct IndexWs {
 int64_t index_slots(int32_t capacity);
 size_t index_ws_bytes(int64_t bq, int32_t capacity);
 IndexWs index_ws_carve(void* ws, int64_t bq, int32_t capacity);
-// the head path (index_head.hip): one to three queries per sequence, and Reindex
+// the head path (index_head.hip): one to three queries per sequence, Reindex, and
+// four or more without a pool
 size_t head_ws_bytes(int64_t bq, int32_t capacity);
 int head_workgroups(bool reindex, int32_t capacity, int64_t bq);
 // the index workspace holds both paths' regions: the shared-load path's first
@@ -88,6 +89,10 @@ hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq
                              const int32_t* q_pos, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
                              int32_t Q, const float* app_kv, const float* app_ik, int32_t app_T, void* ws_head,
                              hipStream_t stream);
+// Full with four or more queries per sequence and no pool: the shared-load
+// scoring with on-chip candidates, then the same exact selection.
+hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, const float* iw, const int32_t* q_pos,
+                                     int32_t* topk_out, int32_t Q, void* ws_head, hipStream_t stream);
 constexpr int kMaxFusedAppend = 8;  // new entries per sequence an indexing launch appends itself
 hipError_t launch_append_index(const LaunchCache& c, const float* kv, const float* ik, int32_t T, const float* iq,
                                const float* iw, const int32_t* q_pos, int32_t* topk_out, int32_t* pool_out,

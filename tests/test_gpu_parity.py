@@ -344,6 +344,84 @@ def test_index_full_prefill_chunk_no_pool(csa, orc):
             topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"topk b{b} q{q}")
 
 
+@pytest.mark.parametrize("Q", [4, 6, 9])  # one workgroup of four queries / of eight (six used) / eight and one
+def test_index_shared_heads_causal(csa, orc, Q):
+    """Four or more queries per sequence without a pool: the queries of a
+    workgroup share its key loads and keep their keys on chip.  Causal
+    positions from before the first entry to past the last, an empty
+    sequence, ratio 2, per-query head weights."""
+    B, cap, ratio = 3, 9003, 2
+    lengths = [9000, 0, 3001]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 31, ratio=ratio)
+    pos = np.array([[-1, 0, 1, 1023, 1024, 8191, 8192, 9999, 17998, 17999],
+                    [-1, 0, 1, 2, 3, 4, 5, 6, 7, 8],
+                    [5, 600, 601, 2047, 6001, 6002, 6003, 100, 4095, 4096]], np.int32)
+    q_pos = np.ascontiguousarray(pos[:, :Q])
+    iq = synth.normal(31, f"iq{Q}", (B, Q, 4, 64))
+    iw = synth.uniform(31, f"iw{Q}", (B, Q, 4), 0.25, 2.0)
+    ref_topk, _, scores = orc.index_topk(oc, orc.FULL, iq, iw=iw, q_pos=q_pos, want_scores=True)
+    gc = upload(csa, oc)
+    topk, _ = run_full(csa, gc, iq, q_pos=q_pos, want_pool=False, iw=iw)
+    swaps = 0
+    for b in range(B):
+        for q in range(Q):
+            n_vis = min(lengths[b], max(0, (int(q_pos[b, q]) + 1) // ratio))
+            if n_vis == 0:
+                assert (topk[b, q] == -1).all(), (b, q)
+            else:
+                swaps += topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"b{b} q{q}")
+    print(f"shared heads, {Q} queries: boundary swaps {swaps}")
+
+
+@pytest.mark.parametrize("lo,n_hot", [(0, 700), (30000, 2000), (61440, 4)])
+def test_index_shared_heads_repair(csa, orc, lo, n_hot):
+    """Clustered high scores for four of five queries that share key loads:
+    the shares holding the hot entries write fewer keys than the Top-512 takes
+    from them, so the select kernel re-scores them with the one-query scoring
+    core (no batch rotation here), which must reproduce the shared scorer's
+    keys bit for bit.  The fifth query has ordinary scores."""
+    B, E, Q = 1, 62000, 5
+    iq1 = synth.normal(32, f"iq{lo}", (1, 1, 4, 64))
+    k = synth.normal_rows(32, f"k{lo}", 0, E, 64) * np.float32(0.05)
+    direction = np.maximum(iq1[0, 0], 0).sum(axis=0) + 1e-3
+    hot = np.arange(lo, min(E, lo + n_hot))
+    ramp = np.linspace(2.0, 3.0, len(hot), dtype=np.float32)[:, None]
+    k[hot] = direction / np.abs(direction).max() * ramp
+    oc = orc.Cache(B, E, 1)
+    oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
+    oc.length[0] = E
+    iq = np.concatenate([np.repeat(iq1, 4, axis=1), synth.normal(32, f"other{lo}", (1, 1, 4, 64))], axis=1)
+    q_pos = np.full((1, Q), E - 1, np.int32)
+    ref, _, scores = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos, want_scores=True)
+    gc = upload(csa, oc)
+    topk, _ = run_full(csa, gc, iq, q_pos=q_pos, want_pool=False)
+    swaps = 0
+    for q in range(Q):
+        swaps += topk_swaps(topk[0, q], ref[0, q], scores[0, q], name=f"q{q}")
+    for q in range(4):
+        assert np.array_equal(topk[0, q], topk[0, 0])
+        assert set(hot[:512].tolist()) <= set(topk[0, q].tolist()) or len(hot) > 512
+    print(f"shared heads clustered {lo}+{n_hot}: {swaps} boundary swaps")
+
+
+@pytest.mark.parametrize("E", [9000, 70000])
+def test_index_shared_heads_relu_zero_ties(csa, orc, E):
+    """Every score of four queries is 0: each share's keys all tie in one bin,
+    more than it may write, so every share is re-scored and the lowest
+    entries win."""
+    B, Q = 1, 4
+    oc = orc.Cache(B, E, 1)
+    k = np.abs(synth.normal_rows(33, "pos", 0, E, 64)) + 0.1
+    oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
+    oc.length[0] = E
+    iq = -np.abs(synth.normal(33, "neg", (1, Q, 4, 64))) - 0.1
+    q_pos = np.full((1, Q), E - 1, np.int32)
+    gc = upload(csa, oc)
+    topk, _ = run_full(csa, gc, iq, q_pos=q_pos, want_pool=False)
+    for q in range(Q):
+        assert np.array_equal(topk[0, q], np.arange(512)), q
+
+
 # selection inside the final kernel / entries through the filter kernel / 8,750 tied pool blocks, more
 # than the candidate buffer holds, selected inside the final kernel
 @pytest.mark.parametrize("E", [9000, 40000, 70000])
@@ -496,18 +574,18 @@ def test_index_reindex(csa, orc, E):
         assert set(got[b, 0].tolist()) == set(ref_full[b, 0].tolist())
 
 
-@pytest.mark.parametrize("Q", [1, 6])  # one-query scorer / eight-query scorer; both through the filter
-def test_index_deterministic(csa, orc, Q):
-    """Repeated calls give identical Top-K lists and pools, although the filter
-    writes its candidates in an order set by atomics."""
+@pytest.mark.parametrize("Q,pool", [(1, True), (6, True), (6, False)])  # one-query / eight-query scorer
+def test_index_deterministic(csa, orc, Q, pool):
+    """Repeated calls give identical Top-K lists and pools, although every
+    path writes its candidates in an order set by atomics."""
     B, E = 2, 30000
     oc = oracle_cache_ik(orc, B, E, [E, E], 25)
     gc = upload(csa, oc)
     iq = synth.normal(25, "iq", (B, Q, 4, 64))
     q_pos = np.array([[E - Q + q for q in range(Q)]] * B, np.int32)
-    a = run_full(csa, gc, iq, q_pos=q_pos)
-    b = run_full(csa, gc, iq, q_pos=q_pos)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    a = run_full(csa, gc, iq, q_pos=q_pos, want_pool=pool)
+    b = run_full(csa, gc, iq, q_pos=q_pos, want_pool=pool)
+    assert np.array_equal(a[0], b[0]) and (not pool or np.array_equal(a[1], b[1]))
 
 
 # ------------------------------------------------------------------ attention
