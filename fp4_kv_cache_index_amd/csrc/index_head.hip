@@ -36,6 +36,8 @@
 // input.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "block_ops.hpp"
 #include "codec.hpp"
 #include "dev_check.hpp"
@@ -705,20 +707,44 @@ struct SelectArgs {
 
 constexpr int kBitWords = 10240;  // the Full output bitmap: ids below 327,680
 
-struct SelectLds {
-  uint64_t set[kHeadCap];  // candidates (then the rank bitmap and its offsets)
+// Sizes of a select kernel instance.  SelAll serves every call.  SelLean
+// serves the Full calls of the shared-load heads with no pool and at most
+// 65,536 visible entries (shares of at most 8 batches): about 71 KB of LDS
+// instead of 150, so that two workgroups share a compute unit when thousands
+// of queries select at once.
+struct SelAll {
+  static constexpr int kSet = kHeadCap;     // candidates held (and the largest key batch)
+  static constexpr int kOut = kPoolBlocks;  // selected keys; boundary-bin keys
+  static constexpr int kIdx = kPoolBlocks;  // share counts (W <= kIdx); wide-range ids
+  static constexpr int kBitW = kBitWords;   // output bitmap words
+  static constexpr int kTake = kBins / 2;   // wide-range buckets
+  static constexpr bool kWide = true;       // the pool kind and ids past the bitmap
+};
+struct SelLean {
+  static constexpr int kSet = 9 * kScoreThreads;  // K kept plus one repaired share of 8 batches
+  static constexpr int kOut = kTopK;
+  static constexpr int kIdx = kScoreThreads;
+  static constexpr int kBitW = 2048;  // ids below 65,536
+  static constexpr int kTake = 1;
+  static constexpr bool kWide = false;
+};
+
+template <class C>
+struct SelectLdsT {
+  using Cfg = C;
+  uint64_t set[C::kSet];  // candidates (then the rank bitmap and its offsets)
   union {
     struct {
-      uint64_t out[kPoolBlocks];  // the selected keys; the boundary bin's keys during a selection
-      uint32_t idx[kPoolBlocks];  // each share's count while loading; ids in the wide-range output
-      uint32_t hist[kBins];       // candidates per bin of their score keys' range
+      uint64_t out[C::kOut];  // the selected keys; the boundary bin's keys during a selection
+      uint32_t idx[C::kIdx];  // each share's count while loading; ids in the wide-range output
+      uint32_t hist[kBins];   // candidates per bin of their score keys' range
     };
-    uint32_t woff[kBitWords];  // Full Top-K output: the selected ids before each bitmap word
+    uint32_t woff[C::kBitW];  // Full Top-K output: the selected ids before each bitmap word
   };
   union {
-    uint32_t bits[kBitWords];  // one bit per selected id (Full)
+    uint32_t bits[C::kBitW];  // one bit per selected id (Full)
     struct {
-      int take[kBins / 2], off[kBins / 2], ge[kBins / 2];  // the wide-range output's buckets
+      int take[C::kTake], off[C::kTake], ge[C::kTake];  // the wide-range output's buckets
     };
   };
   SelShared sel;
@@ -745,13 +771,14 @@ struct KeyBatch {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < N; r++) {
-      const uint64_t v = set[tid + r * kScoreThreads];  // inside L.set: N * 512 <= kHeadCap
+      const uint64_t v = set[tid + r * kScoreThreads];  // inside L.set: N * 512 <= its size
       x[r] = tid + r * kScoreThreads < n ? v : 0ull;
     }
   }
 };
-template <typename F>
+template <int kMaxN, typename F>
 __device__ __forceinline__ void with_keys(const uint64_t* set, int n, F&& f) {
+  static_assert(kMaxN > 8, "the largest batch");
   const int nr = (n + kScoreThreads - 1) / kScoreThreads;  // uniform
   if (nr <= 4) {
     KeyBatch<4> b;
@@ -762,7 +789,7 @@ __device__ __forceinline__ void with_keys(const uint64_t* set, int n, F&& f) {
     b.load(set, n);
     f(b);
   } else {
-    KeyBatch<kHeadCap / kScoreThreads> b;
+    KeyBatch<kMaxN> b;
     b.load(set, n);
     f(b);
   }
@@ -777,11 +804,12 @@ __device__ __forceinline__ void set_bit(uint32_t* bits, uint32_t id) { atomicOr(
 
 // The range [lo, hi] of the score keys (top 32 bits) of the n keys in L.set.
 // Every thread gets it.
-__device__ __forceinline__ void key_range(SelectLds& L, int n, uint32_t& lo, uint32_t& hi) {
+template <class Lds>
+__device__ __forceinline__ void key_range(Lds& L, int n, uint32_t& lo, uint32_t& hi) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   lo = ~0u;
   hi = 0u;
-  with_keys(L.set, n, [&](auto& b) {
+  with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
     for (int r = 0; r < b.kN; r++) {
       const uint32_t x = (uint32_t)(b.x[r] >> 32);
@@ -815,13 +843,15 @@ __device__ __forceinline__ void key_range(SelectLds& L, int n, uint32_t& lo, uin
 // keys (typically one or two) are gathered and ranked exactly (by one wave when
 // there are at most 64 of them, else by the radix select).  Every thread gets
 // S*.
-__device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint32_t lo, uint32_t hi, bool mark) {
+template <class Lds>
+__device__ __forceinline__ uint64_t select_kth(Lds& L, int n, int K, uint32_t lo, uint32_t hi, bool mark) {
+  using C = typename Lds::Cfg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kThr = kScoreThreads;
   // bin of a score key: (x - lo) >> shift, with (hi - lo) >> shift below kBins
   const uint32_t span = hi - lo;
   const int shift = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 12));
-  with_keys(L.set, n, [&](auto& b) {
+  with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
     for (int r = 0; r < b.kN; r++)
       if (b.x[r]) atomicAdd(&L.hist[(((uint32_t)(b.x[r] >> 32)) - lo) >> shift], 1u);
@@ -858,7 +888,7 @@ __device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint3
   const uint32_t bt = (uint32_t)L.bt;
   const int need = K - L.above;  // keys to take from the boundary bin, >= 1
   // the keys of higher bins are taken; the boundary bin's are gathered
-  with_keys(L.set, n, [&](auto& b) {
+  with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
     int nt = 0;
 #pragma unroll
     for (int r = 0; r < b.kN; r++) {
@@ -871,7 +901,7 @@ __device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint3
     for (int r = 0; r < b.kN; r++) {
       const uint32_t bn = (((uint32_t)(b.x[r] >> 32)) - lo) >> shift;
       if (b.x[r] && bn == bt) {
-        if (slot < kPoolBlocks) L.out[slot] = b.x[r];
+        if (slot < C::kOut) L.out[slot] = b.x[r];
         slot++;
       }
     }
@@ -889,11 +919,11 @@ __device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint3
       }
     }
   } else {
-    if (n_tie <= kPoolBlocks && need < n_tie) {
+    if (n_tie <= C::kOut && need < n_tie) {
       int cnt;
       const uint64_t t = topk_threshold<uint64_t>([&](int i) { return L.out[i]; }, n_tie, need, L.sel, &cnt);
       if (tid == 0) L.kth = t;
-    } else if (n_tie <= kPoolBlocks) {  // the whole bin is taken: its smallest key
+    } else if (n_tie <= C::kOut) {  // the whole bin is taken: its smallest key
       uint64_t m = ~0ull;
       for (int i = tid; i < n_tie; i += kThr) m = min(m, L.out[i]);
       m = wave_min(m);
@@ -912,7 +942,7 @@ __device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint3
     if (mark) {  // the boundary bin's keys at or above S*
       __syncthreads();
       const uint64_t kth = L.kth;
-      with_keys(L.set, n, [&](auto& b) {
+      with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
         for (int r = 0; r < b.kN; r++) {
           const uint32_t bn = (((uint32_t)(b.x[r] >> 32)) - lo) >> shift;
@@ -927,9 +957,9 @@ __device__ __forceinline__ uint64_t select_kth(SelectLds& L, int n, int K, uint3
 
 // Re-score share j of query bq exactly as index_head did and append to L.set
 // every key of the kind that the share did not write and that is above s_star.
-template <bool Reindex>
+template <bool Reindex, class Lds>
 __device__ __forceinline__ void repair_share(const SelectArgs& a, int64_t bq, int kind, int j, uint32_t cut, uint64_t s_star,
-                             int32_t n_vis, SelectLds& L) {
+                             int32_t n_vis, Lds& L) {
   const int b = (int)(bq / a.Q);
   const int W = a.W;
   const int lane = threadIdx.x & 63;
@@ -966,15 +996,16 @@ __device__ __forceinline__ void repair_share(const SelectArgs& a, int64_t bq, in
     const uint64_t k64 = key64(key, id);
     const bool add = own && key != 0u && !head_written(key, cut) && k64 > s_star;
     const int slot = wave_slot(add, &L.n);
-    if (add && slot < kHeadCap) L.set[slot] = k64;
+    if (add && slot < Lds::Cfg::kSet) L.set[slot] = k64;
   }
   __syncthreads();
 }
 
 // grid (BQ, kinds): kind 0 writes the Top-512, kind 1 the candidate pool
-template <bool Reindex>
+// (SelAll only; SelLean serves kind 0 with ids below 32 C::kBitW)
+template <bool Reindex, class C>
 __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs a) {
-  __shared__ SelectLds L;
+  __shared__ SelectLdsT<C> L;
   constexpr int kThr = kScoreThreads;
   const int64_t bq = blockIdx.x;
   const int kind = blockIdx.y;
@@ -988,15 +1019,15 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   const uint32_t* cuts = a.ws.cut + (bq * 2 + kind) * a.ws.wstride;
   // ids of the output: entries or blocks (Full), pool slots (Reindex)
   const int64_t universe = Reindex ? (int64_t)kPool : (kind == 0 ? (int64_t)n_vis : ((int64_t)n_vis + kBlock - 1) / kBlock);
-  const bool direct = universe <= 32 * (int64_t)kBitWords;  // uniform: the bitmap output
+  const bool direct = !C::kWide || universe <= 32 * (int64_t)C::kBitW;  // uniform: the bitmap output
   const int nw = direct ? (int)((universe + 31) >> 5) : 0;
 
   // ---- the first R slots of every stretch (speculatively), the counts and the
   // floors, all at once: thread t holds slot pairs p = t + 512 u (pair p is
   // slots 2 (p mod R/2) and one more of stretch p div R/2), counts and floors of
-  // shares t + 512 f (W <= 2048)
-  constexpr int kPairs = kHeadCap / (2 * kThr);
-  constexpr int kFl = 4;
+  // shares t + 512 f (W <= C::kIdx)
+  constexpr int kPairs = (C::kSet / 2 + kThr - 1) / kThr;  // W tc <= C::kSet
+  constexpr int kFl = C::kIdx / kThr;
   const int R = a.spec[kind], rh = R >> 1;
   const uint32_t rh_magic = a.spec_magic[kind];
   const uint32_t npairs = (uint32_t)W * (uint32_t)rh;
@@ -1184,7 +1215,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
         __syncthreads();
       }
       repair_share<Reindex>(a, bq, kind, gj, cuts[gj], s_star, n_vis, L);
-      if (tid == 0 && L.n > kHeadCap) L.n = kHeadCap;  // never reached: at most K kept plus one share's keys
+      if (tid == 0 && L.n > C::kSet) L.n = C::kSet;  // never reached: at most K kept plus one share's keys
       __syncthreads();
 #pragma unroll
       for (int f = 0; f < kFl; f++)
@@ -1205,12 +1236,12 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
     }
   }
 
-  constexpr int kR = kHeadCap / kThr;  // candidates per thread at most
+  constexpr int kR = C::kSet / kThr;  // candidates per thread at most
   if (direct) {
     // ---- Full: one bit per selected id, then each thread writes the ids of its
     // words in ascending order from its offset
     if (!marked) {  // uniform
-      with_keys(L.set, n, [&](auto& b) {
+      with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
         for (int r = 0; r < b.kN; r++)
           if (b.x[r] && b.x[r] >= s_star) set_bit(L.bits, key_id(b.x[r]));  // ids below universe
@@ -1227,7 +1258,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < N; i++) {
-        const uint32_t v = L.bits[w0 + i];  // inside L.bits: 512 N <= kBitWords
+        const uint32_t v = L.bits[w0 + i];  // inside L.bits: 512 N <= C::kBitW
         wd[i] = w0 + i < nw ? v : 0u;
         cnt += __popc(wd[i]);
       }
@@ -1246,7 +1277,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
         // is entry order, and the slot's entry is written)
         int32_t* dst = a.topk_out + bq * kTopK;
         const int32_t* pool = Reindex ? a.pool_in + bq * kPool : nullptr;
-        with_keys(L.set, n, [&](auto& b) {
+        with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
           for (int r = 0; r < b.kN; r++) {
             if (b.x[r] && b.x[r] >= s_star) {
@@ -1260,7 +1291,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
           }
         });
         for (int i = nsel + tid; i < kTopK; i += kThr) dst[i] = -1;
-      } else {
+      } else if constexpr (C::kWide) {
         // the chosen blocks in ascending order into L.idx, then each expanded to
         // its visible entries (every chosen block is full except possibly the one
         // holding the last visible entry, so block r of the order fills slots
@@ -1291,20 +1322,24 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
         }
       }
     };
-    const int wpt = (nw + kThr - 1) / kThr;  // uniform
-    if (wpt <= 1)
+    const int wpt = (nw + kThr - 1) / kThr;  // uniform, at most C::kBitW / kThr
+    if (wpt <= 1) {
       emit(IntC<1>{});
-    else if (wpt <= 2)
+    } else if (wpt <= 2) {
       emit(IntC<2>{});
-    else if (wpt <= 4)
+    } else if (wpt <= 4) {
       emit(IntC<4>{});
-    else if (wpt <= 8)
-      emit(IntC<8>{});
-    else if (wpt <= 16)
-      emit(IntC<16>{});
-    else
-      emit(IntC<kBitWords / kScoreThreads>{});
-  } else {
+    } else {
+      if constexpr (C::kBitW / kScoreThreads > 4) {
+        if (wpt <= 8)
+          emit(IntC<8>{});
+        else if (wpt <= 16)
+          emit(IntC<16>{});
+        else
+          emit(IntC<C::kBitW / kScoreThreads>{});
+      }
+    }
+  } else if constexpr (C::kWide) {
     // ---- the selected keys: every candidate at or above S*, one LDS atomic per wave
     if (tid == 0) L.n_out = 0;
     __syncthreads();
@@ -1421,21 +1456,24 @@ CSA2_DEV_ERROR_TAKER(take_head_dev_error)
 // keys in the kernel) and the most it may write (the query's kHeadCap split
 // evenly).  A share holding more of the Top-K than it wrote is re-scored by
 // the select kernel.
-static void head_targets(int W, int K, int32_t& T, int32_t& T_cap) {
-  T_cap = (kHeadCap / W) & ~1;  // even: the select kernel loads slot pairs
+static void head_targets(int W, int K, int32_t& T, int32_t& T_cap, int cap_total = kHeadCap) {
+  T_cap = (cap_total / W) & ~1;  // even: the select kernel loads slot pairs
   const int want = (3 * K + 2 * W - 1) / (2 * W) + 16;
   T = want < T_cap ? want : T_cap;
 }
 
-// The select kernel over the heads of W shares per query (iters batches each).
+// The select kernel over the heads of W shares per query (iters batches each);
+// `lean`: the SelLean instance (kind 0, ids below 65,536, at most 8 batches a
+// share), whose stretches hold SelLean::kSet / W keys.
 static hipError_t launch_select(const LaunchCache& c, bool reindex, const float* iq, const float* iw,
                                 const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out, int32_t Q, int W,
-                                int iters, int32_t app_T, int rotate, int kinds, const HeadWs& ws,
+                                int iters, int32_t app_T, int rotate, int kinds, const HeadWs& ws, bool lean,
                                 hipStream_t stream) {
   const int64_t bq = (int64_t)c.batch * Q;
   int32_t T[2], T_cap[2];
-  head_targets(W, kTopK, T[0], T_cap[0]);
-  head_targets(W, kPoolBlocks, T[1], T_cap[1]);
+  const int cap_total = lean ? SelLean::kSet : kHeadCap;
+  head_targets(W, kTopK, T[0], T_cap[0], cap_total);
+  head_targets(W, kPoolBlocks, T[1], T_cap[1], cap_total);
   SelectArgs s;
   s.ik_codes = c.ik_codes;
   s.ik_scales = c.ik_scales;
@@ -1462,9 +1500,11 @@ static hipError_t launch_select(const LaunchCache& c, bool reindex, const float*
   s.pool_out = reindex ? nullptr : pool_out;
   const dim3 sgrid((unsigned)bq, (unsigned)kinds);
   if (reindex)
-    hipLaunchKernelGGL(index_select_kernel<true>, sgrid, dim3(kScoreThreads), 0, stream, s);
+    hipLaunchKernelGGL((index_select_kernel<true, SelAll>), sgrid, dim3(kScoreThreads), 0, stream, s);
+  else if (lean)
+    hipLaunchKernelGGL((index_select_kernel<false, SelLean>), sgrid, dim3(kScoreThreads), 0, stream, s);
   else
-    hipLaunchKernelGGL(index_select_kernel<false>, sgrid, dim3(kScoreThreads), 0, stream, s);
+    hipLaunchKernelGGL((index_select_kernel<false, SelAll>), sgrid, dim3(kScoreThreads), 0, stream, s);
   return hipGetLastError();
 }
 
@@ -1512,7 +1552,7 @@ hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_select(c, reindex, iq, iw, pool_in, topk_out, pool_out, Q, h.W, h.iters, app_T, 1, kinds, h.ws,
-                       stream);
+                       false, stream);
 }
 
 // Full with four or more queries per sequence and no pool: the shared-load
@@ -1538,14 +1578,17 @@ hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, cons
   h.W = shared_head_workgroups(c.capacity);
   const int64_t batches = ((int64_t)c.capacity + kBatchKeys - 1) / kBatchKeys;
   h.iters = (int32_t)((batches + h.W - 1) / h.W);  // at most kSharedIters
+  // the lean select serves ids below 65,536 (every query's visible entries
+  // are at most the capacity)
+  const bool lean = c.capacity <= 32 * SelLean::kBitW;
   int32_t T;
-  head_targets(h.W, kTopK, T, h.T_cap);
+  head_targets(h.W, kTopK, T, h.T_cap, lean ? SelLean::kSet : kHeadCap);
   h.ws = head_ws_carve(ws_head, bq, c.capacity);
   const dim3 grid((unsigned)(c.batch * ((Q + qpw - 1) / qpw)), (unsigned)h.W);
   hipLaunchKernelGGL(index_shared_head_kernel<1>, grid, dim3(kScoreThreads), 0, stream, h);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_select(c, false, iq, iw, nullptr, topk_out, nullptr, Q, h.W, h.iters, 0, 0, 1, h.ws, stream);
+  return launch_select(c, false, iq, iw, nullptr, topk_out, nullptr, Q, h.W, h.iters, 0, 0, 1, h.ws, lean, stream);
 }
 
 }  // namespace csa2
