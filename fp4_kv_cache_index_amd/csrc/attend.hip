@@ -437,6 +437,90 @@ __device__ __forceinline__ void attend_block(const Wg& w, int j, int grp, const 
   }
 }
 
+constexpr int kPStride = 72;  // fp16 per head row of the shared P tile (64 keys + pad)
+
+// attend_block with the block's softmax split over the waves (many queries:
+// two workgroups per compute unit, where VALU work, not a barrier, sets the
+// pace): wave w takes heads 4w .. 4w+3, four keys per lane, and shares P (fp16)
+// and each head's rescale factor through LDS (s_p, s_alpha).  This wave's
+// running (m_run, l_run) are those of head 4 wave + lane / 16; the output
+// rows of this lane's accumulators are head n = lane % 16.  The same values
+// as attend_block, but for the order of each head's sum over a block.
+__device__ __forceinline__ void attend_block_sp(const Wg& w, int j, int grp, const Raw& cur, int32_t id_c,
+                                                const v8h (&qb)[16], float qfac, const uint8_t* s_new, _Float16* s_v,
+                                                float* s_s, _Float16* s_p, float* s_alpha, v4f (&acc)[8], float& m_run,
+                                                float& l_run) {
+  const int n = w.n, g = w.g, wave = w.wave;
+  const int lane = w.tid & 63;
+  const uint32_t vmask = (uint32_t)__ballot(key_valid(w, grp, id_c)) & 0xFFFFu;  // bit k: key k exists
+  if (j > 0) lds_barrier();  // every wave is done with the previous block's tile, scores and P
+  v4f st = {0.f, 0.f, 0.f, 0.f};
+  _Float16* rows = s_v + wave * 16 * kVStride + n * kVStride + 128 * g;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    uint32_t kh[32];
+    dequant(w, grp, cur, s_new, h, kh);
+#pragma unroll
+    for (int kb = 0; kb < 8; kb++) {
+      const v8h ka = __builtin_bit_cast(v8h, make_uint4(kh[4 * kb], kh[4 * kb + 1], kh[4 * kb + 2], kh[4 * kb + 3]));
+      st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[8 * h + kb], st, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; c++)
+      *reinterpret_cast<uint4*>(rows + 64 * h + 8 * c) = make_uint4(kh[4 * c], kh[4 * c + 1], kh[4 * c + 2], kh[4 * c + 3]);
+  }
+  {
+    v4f sc;
+#pragma unroll
+    for (int i = 0; i < 4; i++) sc[i] = ((vmask >> (4 * g + i)) & 1u) ? st[i] * qfac : -INFINITY;
+    *reinterpret_cast<v4f*>(s_s + n * kSStride + 16 * wave + 4 * g) = sc;
+  }
+  lds_barrier();  // every wave's scores and keys are in
+
+  // ---- softmax of head hs = 4 wave + lane / 16 over the block: keys 4 (lane % 16) .. +3
+  {
+    const int hs = 4 * wave + (lane >> 4), k0 = 4 * (lane & 15);
+    const v4f sv = *reinterpret_cast<const v4f*>(s_s + hs * kSStride + k0);
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = wave_row_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
+    float ps = 0.0f;
+    v4h pv;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float e = sv[i] == -INFINITY ? 0.0f : __expf(sv[i] - m_new);
+      ps += e;
+      pv[i] = (_Float16)e;
+    }
+    ps = wave_row_reduce(ps, [](float x, float y) { return x + y; });
+    m_run = m_new;
+    l_run = alpha * l_run + ps;
+    *reinterpret_cast<v4h*>(s_p + hs * kPStride + k0) = pv;
+    if ((lane & 15) == 0) s_alpha[hs] = alpha;
+  }
+  lds_barrier();  // P and every head's rescale factor are in
+
+  // ---- O^T = alpha O^T + V^T P^T for channels 128 wave .. +127, head n
+  const float alpha_n = s_alpha[n];
+  v8h pb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) pb[kb] = *reinterpret_cast<const v8h*>(s_p + n * kPStride + 32 * kb + 8 * g);
+#pragma unroll
+  for (int c = 0; c < 8; c++) acc[c] *= alpha_n;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++) {
+    const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const v4h lo = lds_read_tr16(vsrc + 16 * c);
+      const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
+      const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
+    }
+  }
+}
+
 // The query staged in LDS (s_q, s_qfac) and the new window tokens (s_new);
 // returns the query operand of S^T = K Q^T in qb: head n, channels 128g + 8kb .. +7.
 __device__ __forceinline__ void attend_setup(const Wg& w, const AttnArgs& a, const uint4 (&qraw)[4],
@@ -494,10 +578,15 @@ __device__ __forceinline__ void attend_finish(const Wg& w, const AttnArgs& a, co
 template <int kGpw>  // blocks per workgroup
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) attend_block_kernel(AttnArgs a) {
   static_assert(16 * kQStride <= kWaves * 16 * kVStride, "the query staging fits in the key tile");
+  // the softmax split over the waves where a workgroup takes every block of its query
+  constexpr bool kShareP = kGpw == 10;
   __shared__ __attribute__((aligned(16))) _Float16 s_v[kWaves * 16 * kVStride];  // query staging, then keys
   __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
   __shared__ float s_qfac[16];
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[kShareP ? 16 * kPStride : 8];  // P [head][key]
+  __shared__ float s_alpha[16];
+  __shared__ float2 s_ml[16];
   const Wg w = make_wg(a, kGpw);
   const int grp0 = w.split * kWaves * kGpw + w.wave;  // block j: group grp0 + 4j
 
@@ -523,7 +612,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const int grp = grp0 + kWaves * j;
     const int32_t id_n2 = load_id(w, j + 2 < kGpw ? grp + 2 * kWaves : kMainGroups);
     issue(w, a, grp + kWaves, id_n, nxt, j + 1 < kGpw);
-    attend_block(w, j, grp, cur, id_c, qb, qfac, s_new, s_v, s_s, acc, m_run, l_run);
+    if constexpr (kShareP)
+      attend_block_sp(w, j, grp, cur, id_c, qb, qfac, s_new, s_v, s_s, s_p, s_alpha, acc, m_run, l_run);
+    else
+      attend_block(w, j, grp, cur, id_c, qb, qfac, s_new, s_v, s_s, acc, m_run, l_run);
     return id_n2;
   };
 #pragma unroll 1
@@ -534,6 +626,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       id_a = id_c;
       id_b = id_d;
     }
+  }
+  if constexpr (kShareP) {  // head n's (max, sum) from the wave that took its softmax
+    if (((w.tid & 63) & 15) == 0) s_ml[4 * w.wave + ((w.tid & 63) >> 4)] = make_float2(m_run, l_run);
+    lds_barrier();
+    const float2 ml = s_ml[w.n];
+    m_run = ml.x;
+    l_run = ml.y;
   }
   attend_finish(w, a, acc, m_run, l_run);
 }

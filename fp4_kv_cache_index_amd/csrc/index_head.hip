@@ -129,6 +129,10 @@ __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (u
 
 // a key of a share is written to the candidates iff it is nonzero and its bin
 // is above the share's cut bin, or equal to it when that bin was written
+// max(x, 0) for a finite x, as one integer max on its bits (a negative float
+// is a negative integer; -0 gives +0)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ bool head_written(uint32_t x, uint32_t cut) {
   const uint32_t bn = x >> kBinShift, bt = cut >> 1;
   return x != 0u && (bn > bt || (bn == bt && (cut & 1u)));
@@ -468,7 +472,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   __shared__ uint32_t s_hist[kQ][kBins / 2];
   __shared__ __attribute__((aligned(16))) uint8_t s_q8[kQ][256];
   __shared__ float s_c[kQ][4];
-  __shared__ uint32_t s_max[kQ], s_live[kQ], s_cut[kQ];
+  __shared__ uint32_t s_max[kQ], s_cut[kQ];
   __shared__ uint32_t s_n[kQ];
   __shared__ unsigned long long s_floor[kQ];
 
@@ -508,18 +512,25 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   }
 
   const int64_t row_base = (int64_t)b * a.cap;
-  const BufRsrc kr = make_rsrc(a.ik_codes + row_base * 64, (uint32_t)nv_max * 64u);
-  const BufRsrc sr = make_rsrc(a.ik_scales + row_base, (uint32_t)nv_max * 4u);
+  // a lane's key of group jj in a batch is entry base + loff[jj]
+  uint32_t loff[kBatch];
+#pragma unroll
+  for (int jj = 0; jj < kBatch; jj++) loff[jj] = (uint32_t)(16 * (jj * kScoreWaves + wave) + row);
   auto base_of = [&](int it) -> int64_t { return head_batch(j, it, W, a.iters, 0) * kBatchKeys; };
   // batches ascend with it, so the live ones come first
   auto live = [&](int it) -> bool { return it < a.iters && base_of(it) < nv_max; };  // uniform
+  // a live batch's loads: its base goes into the buffer descriptors (bounded
+  // at the largest visible count), so the per-lane offsets stay fixed
   auto issue = [&](int it, v4i (&bytes)[kBatch], float (&sk)[kBatch]) {
     const int64_t base = base_of(it);
+    const int64_t left = (int64_t)nv_max - base;
+    const uint32_t nrec = left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys;
+    const BufRsrc kb = make_rsrc(a.ik_codes + (row_base + base) * 64, nrec * 64u);
+    const BufRsrc sb = make_rsrc(a.ik_scales + (row_base + base), nrec * 4u);
 #pragma unroll
     for (int jj = 0; jj < kBatch; jj++) {
-      const uint32_t e = (uint32_t)(base + 16 * (jj * kScoreWaves + wave) + row);
-      bytes[jj] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kr, e * 64u + 16u * grp, 0, kNT));
-      sk[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, e * 4u, 0, 0));
+      bytes[jj] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kb, loff[jj] * 64u + 16u * grp, 0, kNT));
+      sk[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sb, loff[jj] * 4u, 0, 0));
     }
   };
   v4i bytes[2][kBatch];
@@ -530,7 +541,6 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   for (int i = tid; i < kQ * kBins / 2; i += kScoreThreads) (&s_hist[0][0])[i] = 0u;
   if (tid < kQ) {
     s_max[tid] = 0u;
-    s_live[tid] = 0u;
     s_n[tid] = 0u;
     s_floor[tid] = 0ull;
   }
@@ -566,9 +576,9 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   }
 
   uint32_t ks[kSharedIters][kBatch][G];  // this lane's keys: batch, group, query 4g + jq
-  uint32_t kmax[G], nlive[G];
+  uint32_t kmax[G];
 #pragma unroll
-  for (int g = 0; g < G; g++) kmax[g] = nlive[g] = 0u;
+  for (int g = 0; g < G; g++) kmax[g] = 0u;
 #pragma unroll
   for (int it = 0; it < kSharedIters; it++) {
 #pragma unroll
@@ -577,38 +587,39 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
       for (int g = 0; g < G; g++) ks[it][jj][g] = 0u;
     if (it >= 1 && it + 1 < kSharedIters && live(it + 1)) issue(it + 1, bytes[(it + 1) & 1], sk[(it + 1) & 1]);
     if (!live(it)) continue;  // uniform
-    const int64_t base = base_of(it);
+    const int32_t sbase = (int32_t)base_of(it);
     const v4i(&by)[kBatch] = bytes[it & 1];
 #pragma unroll
     for (int jj = 0; jj < kBatch; jj++) {
       const v8bf k0 = widen8((uint32_t)by[jj][0], (uint32_t)by[jj][1]);
       const v8bf k1 = widen8((uint32_t)by[jj][2], (uint32_t)by[jj][3]);
-      const int64_t e = base + 16 * (jj * kScoreWaves + wave) + row;
+      const int32_t e = sbase + (int32_t)loff[jj];
 #pragma unroll
       for (int g = 0; g < G; g++) {
         v4f d = {0.f, 0.f, 0.f, 0.f};
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0[g], k0, d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1[g], k1, d, 0, 0, 0);
+        // the one-query core's arithmetic, in fewer instructions: ReLU as an
+        // integer max (finite inputs: d > 0 keeps d, else +0), and the scale
+        // as an fma with +0, which turns a -0 product into +0 so that the
+        // order key needs no -0 case (order_key maps both zeros alike)
         float acc = 0.0f;
-        acc = __builtin_fmaf(ch[g][0], d[0] > 0.0f ? d[0] : 0.0f, acc);
-        acc = __builtin_fmaf(ch[g][1], d[1] > 0.0f ? d[1] : 0.0f, acc);
-        acc = __builtin_fmaf(ch[g][2], d[2] > 0.0f ? d[2] : 0.0f, acc);
-        acc = __builtin_fmaf(ch[g][3], d[3] > 0.0f ? d[3] : 0.0f, acc);
-        const uint32_t key = e < my_nv[g] ? order_key(sk[it & 1][jj] * acc) : 0u;
+        acc = __builtin_fmaf(ch[g][0], relu_bits(d[0]), acc);
+        acc = __builtin_fmaf(ch[g][1], relu_bits(d[1]), acc);
+        acc = __builtin_fmaf(ch[g][2], relu_bits(d[2]), acc);
+        acc = __builtin_fmaf(ch[g][3], relu_bits(d[3]), acc);
+        const uint32_t u = __float_as_uint(__builtin_fmaf(sk[it & 1][jj], acc, 0.0f));
+        const uint32_t key = e < my_nv[g] ? (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) : 0u;
         ks[it][jj][g] = key;
         kmax[g] = max(kmax[g], key);
-        nlive[g] += key != 0u ? 1u : 0u;
         const uint32_t bin = key >> kBinShift;
-        if (key) atomicAdd(&s_hist[4 * g + jq][bin >> 1], 1u << (16 * (bin & 1u)));
+        atomicAdd(&s_hist[4 * g + jq][bin >> 1], key ? 1u << (16 * (bin & 1u)) : 0u);  // 0: no key, adds nothing
       }
     }
   }
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    if (4 * g + jq < nq) {
-      atomicMax(&s_max[4 * g + jq], kmax[g]);
-      atomicAdd(&s_live[4 * g + jq], nlive[g]);
-    }
+    if (4 * g + jq < nq) atomicMax(&s_max[4 * g + jq], kmax[g]);
   }
   __syncthreads();  // the histograms, maxima and counts are complete
 
@@ -618,7 +629,12 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
     int32_t total = 0;
 #pragma unroll
     for (int u = 0; u < kQ; u++) total = u == wave ? nv[u] : total;
-    const uint32_t lv = s_live[wave];
+    // the share's keys of the query: its visible entries among the share's batches
+    uint32_t lv = 0u;
+    for (int it = 0; it < a.iters; it++) {
+      const int64_t left = (int64_t)total - base_of(it);
+      lv += left <= 0 ? 0u : (left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys);
+    }
     const int64_t want = total > 0 ? (3 * (int64_t)kTopK * lv + 2 * (int64_t)total - 1) / (2 * (int64_t)total) + 16 : 0;
     const int T = (int)min(want, (int64_t)a.T_cap);
     const uint32_t* h = s_hist[wave];
@@ -632,9 +648,6 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   // thr is the cut bin's lowest key when that bin is written, else the next
   // bin's, and at least 1); ids ascend with (it, jj) in a lane, so the first
   // unwritten key of the largest value has the lowest id.
-  uint32_t loff[kBatch];
-#pragma unroll
-  for (int jj = 0; jj < kBatch; jj++) loff[jj] = (uint32_t)(16 * (jj * kScoreWaves + wave) + row);
 #pragma unroll
   for (int g = 0; g < G; g++) {
     const int jx = 4 * g + jq;
