@@ -619,7 +619,7 @@ def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
     if head is None:
         head = next(w for w in synth.WORKLOADS.values() if w["name"] == workload_name).get("Q", 1) < 4
     if head:
-        parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false>", True))
+        parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false, csa2::SelAll>", True))
     else:
         parts = (("score", "index_scoreq_kernel<", False), ("filter", "index_filter_kernel", False),
                  ("final", "index_final_kernel", True))
@@ -854,8 +854,10 @@ def main():
     traffic = traffic_from_profiles(wl, "index_full")
     if getattr(wl, "Q", 1) < 4:
         kernel_name = "index_head + index_select (one csa2_index_score_topk Full call)"
+    elif "full_pool" not in getattr(wl, "group", ()):
+        kernel_name = "index_shared_head + index_select (one csa2_index_score_topk Full call)"
     else:
-        kernel_name = "index_score + index_filter + index_final (one csa2_index_score_topk Full call)"
+        kernel_name = "index_scoreq + index_filter + index_final (one csa2_index_score_topk Full call)"
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_GBPS * 1e9)  # FLOP per byte where the bf16 matrix cores take over
     if flops / idx_bytes < ridge:
         # decode (one or a few queries per sequence): bound by streaming the indexer keys

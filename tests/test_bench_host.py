@@ -99,12 +99,12 @@ def test_counter_summary_decode_kernels(tmp_path, monkeypatch):
 
     copy = "__amd_rocclr_copyBuffer"
     fetch = [("void csa2::index_head_kernel<false>(csa2::HeadArgs)", 262144, 70000.0),
-             ("void csa2::index_select_kernel<false>(csa2::SelectArgs)", 16384, 900.0),
+             ("void csa2::index_select_kernel<false, csa2::SelAll>(csa2::SelectArgs)", 16384, 900.0),
              ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 11000.0),
-             ("void csa2::index_select_kernel<true>(csa2::SelectArgs)", 8192, 600.0),
+             ("void csa2::index_select_kernel<true, csa2::SelAll>(csa2::SelectArgs)", 8192, 600.0),
              (copy, 65536, 131072.0), (copy, 65536, 131072.0), (copy, 65536, 131072.0)]
     write = [("void csa2::index_head_kernel<false>(csa2::HeadArgs)", 262144, 800.0),
-             ("void csa2::index_select_kernel<false>(csa2::SelectArgs)", 16384, 1000.0),
+             ("void csa2::index_select_kernel<false, csa2::SelAll>(csa2::SelectArgs)", 16384, 1000.0),
              ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 150.0),
              (copy, 65536, 262144.0), (copy, 65536, 262144.0), (copy, 65536, 262144.0)]
     f = tmp_path / "fetch.csv"
