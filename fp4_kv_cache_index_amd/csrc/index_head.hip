@@ -208,24 +208,34 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     const int T = (int)min(want, (int64_t)T_cap[kind]);
     const uint32_t* hist = kind ? hist1 : hist0;
     const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
-    // this lane's written keys and the largest unwritten one
-    uint32_t mine = 0u;
-    uint64_t fl = 0ull;
+    // head_written as one compare: a key x is written iff x >= thr (the cut
+    // bin's lowest key when that bin is written, else the next bin's, and at
+    // least 1); nothing is written when that is past the top bin
+    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
+    const bool any = thr64 <= 0xFFFFFFFFull;
+    const uint32_t thr = thr64 > 1ull ? (uint32_t)thr64 : 1u;
+    // this lane's written keys and the largest unwritten one (the lowest id
+    // among equal keys), kept as a 32-bit key and its id
+    uint32_t mine = 0u, fx = 0u, fid = 0xFFFFFFFFu;
 #pragma unroll
     for (int it = 0; it < kIters; it++) {
       const uint32_t x = ks[kind][it];
-      const bool w = head_written(x, cut);
+      const bool w = any && x >= thr;
       mine += w ? 1u : 0u;
-      const uint64_t k = (x != 0u && !w) ? key64(x, idf(kind, it)) : 0ull;
-      fl = k > fl ? k : fl;
+      const uint32_t xu = w ? 0u : x;
+      const uint32_t id = idf(kind, it);
+      const bool up = xu > fx || (xu == fx && id < fid);
+      fx = up ? xu : fx;
+      fid = up ? id : fid;
     }
+    uint64_t fl = fx ? key64(fx, fid) : 0ull;
     // one LDS atomic per wave reserves its slots in the share's stretch
     uint32_t slot = (uint32_t)wave_alloc((int)mine, &H.n[kind]);
     uint64_t* dst = cand + kind * kHeadCap + (int64_t)j * T_cap[kind];
 #pragma unroll
     for (int it = 0; it < kIters; it++) {
       const uint32_t x = ks[kind][it];
-      const bool w = head_written(x, cut);
+      const bool w = any && x >= thr;
       if (w && slot < (uint32_t)T_cap[kind]) dst[slot] = key64(x, idf(kind, it));  // the cap always holds
       slot += w ? 1u : 0u;
     }
