@@ -182,8 +182,8 @@ __device__ uint32_t head_cut(CountF count_of, uint32_t mx, int T, int T_cap) {
 // batch it (0 = none; a block key is held by lane 8b of its block only);
 // idf(kind, it): the key's id.  H.wmax and H.wlive hold every wave's largest
 // key and count of keys, and H.n is zero (the caller has synchronised after the
-// histograms).  The share wants T = 1.5 K live / total + 16 keys of a kind: one
-// and a half times its share of the K selected, in proportion to its keys
+// histograms).  The share wants T = 1.25 K live / total + 16 keys of a kind:
+// a quarter more than its share of the K selected, in proportion to its keys
 // among the query's `total` (a Reindex pool shorter than its slots leaves most
 // shares empty); T_cap: most keys a share may write.  Out-pointers are kind
 // 0's; kind 1's follow at `stride`.
@@ -204,7 +204,7 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
       live += H.wlive[kind][w];
     }
     const int64_t K = kind ? kPoolBlocks : kTopK;
-    const int64_t want = total[kind] > 0 ? (3 * K * live + 2 * total[kind] - 1) / (2 * total[kind]) + 16 : 0;
+    const int64_t want = total[kind] > 0 ? (5 * K * live + 4 * total[kind] - 1) / (4 * total[kind]) + 16 : 0;
     const int T = (int)min(want, (int64_t)T_cap[kind]);
     const uint32_t* hist = kind ? hist1 : hist0;
     const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
@@ -645,7 +645,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
       const int64_t left = (int64_t)total - base_of(it);
       lv += left <= 0 ? 0u : (left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys);
     }
-    const int64_t want = total > 0 ? (3 * (int64_t)kTopK * lv + 2 * (int64_t)total - 1) / (2 * (int64_t)total) + 16 : 0;
+    const int64_t want = total > 0 ? (5 * (int64_t)kTopK * lv + 4 * (int64_t)total - 1) / (4 * (int64_t)total) + 16 : 0;
     const int T = (int)min(want, (int64_t)a.T_cap);
     const uint32_t* h = s_hist[wave];
     const uint32_t cut = head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
@@ -762,10 +762,10 @@ struct SelectLdsT {
       uint32_t idx[C::kIdx];  // each share's count while loading; ids in the wide-range output
       uint32_t hist[kBins];   // candidates per bin of their score keys' range
     };
-    uint32_t woff[C::kBitW];  // Full Top-K output: the selected ids before each bitmap word
+    uint32_t woff[C::kBitW + C::kBitW / 8];  // Full Top-K output: the selected ids before each bitmap word (padded)
   };
   union {
-    uint32_t bits[C::kBitW];  // one bit per selected id (Full)
+    uint32_t bits[C::kBitW + C::kBitW / 8];  // one bit per selected id (Full; padded words)
     struct {
       int take[C::kTake], off[C::kTake], ge[C::kTake];  // the wide-range output's buckets
     };
@@ -823,7 +823,13 @@ struct IntC {
   static constexpr int value = N;
 };
 
-__device__ __forceinline__ void set_bit(uint32_t* bits, uint32_t id) { atomicOr(&bits[id >> 5], 1u << (id & 31u)); }
+// Output bitmaps hold word w at w + w / 8: a thread that owns eight
+// consecutive words then reads and writes them without LDS bank conflicts
+// (lanes 9 words apart instead of 8).
+__device__ __forceinline__ int bw(int w) { return w + (w >> 3); }
+__device__ __forceinline__ void set_bit(uint32_t* bits, uint32_t id) {
+  atomicOr(&bits[bw((int)(id >> 5))], 1u << (id & 31u));
+}
 
 // The range [lo, hi] of the score keys (top 32 bits) of the n keys in L.set.
 // Every thread gets it.
@@ -1074,7 +1080,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   }
   // the histogram and the bitmap start clear
   for (int i = tid; i < kBins; i += kThr) L.hist[i] = 0u;
-  for (int i = tid; i < nw; i += kThr) L.bits[i] = 0u;
+  for (int i = tid; i < bw(nw); i += kThr) L.bits[i] = 0u;
   uint64_t fmax = 0ull;
   bool over = false;
 #pragma unroll
@@ -1254,7 +1260,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
       }
     }
     if (direct) {
-      for (int i = tid; i < nw; i += kThr) L.bits[i] = 0u;
+      for (int i = tid; i < bw(nw); i += kThr) L.bits[i] = 0u;
       __syncthreads();
     }
   }
@@ -1281,7 +1287,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < N; i++) {
-        const uint32_t v = L.bits[w0 + i];  // inside L.bits: 512 N <= C::kBitW
+        const uint32_t v = L.bits[bw(w0 + i)];  // inside L.bits: 512 N <= C::kBitW
         wd[i] = w0 + i < nw ? v : 0u;
         cnt += __popc(wd[i]);
       }
@@ -1292,7 +1298,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
         // plus the set bits below it in the word
 #pragma unroll
         for (int i = 0; i < N; i++) {
-          if (w0 + i < nw) L.woff[w0 + i] = (uint32_t)pos;
+          if (w0 + i < nw) L.woff[bw(w0 + i)] = (uint32_t)pos;
           pos += __popc(wd[i]);
         }
         __syncthreads();
@@ -1306,7 +1312,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
             if (b.x[r] && b.x[r] >= s_star) {
               const uint32_t id = key_id(b.x[r]);
               const uint32_t w = id >> 5;
-              const int rank = (int)L.woff[w] + __popc(L.bits[w] & ((1u << (id & 31u)) - 1u));
+              const int rank = (int)L.woff[bw((int)w)] + __popc(L.bits[bw((int)w)] & ((1u << (id & 31u)) - 1u));
               int32_t v = (int32_t)id;
               if (Reindex) v = (pf_ok && r < kPf) ? pe[r < kPf ? r : 0] : pool[id];
               if (rank < kTopK) dst[rank] = v;
@@ -1474,14 +1480,14 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
 // ------------------------------------------------------------------ launch
 CSA2_DEV_ERROR_TAKER(take_head_dev_error)
 
-// per share: the keys wanted when every share holds as many keys (one and a
-// half times its even share of K, plus 16; each share scales this by its own
+// per share: the keys wanted when every share holds as many keys (1.25 times
+// its even share of K, plus 16; each share scales this by its own
 // keys in the kernel) and the most it may write (the query's kHeadCap split
 // evenly).  A share holding more of the Top-K than it wrote is re-scored by
 // the select kernel.
 static void head_targets(int W, int K, int32_t& T, int32_t& T_cap, int cap_total = kHeadCap) {
   T_cap = (cap_total / W) & ~1;  // even: the select kernel loads slot pairs
-  const int want = (3 * K + 2 * W - 1) / (2 * W) + 16;
+  const int want = (5 * K + 4 * W - 1) / (4 * W) + 16;
   T = want < T_cap ? want : T_cap;
 }
 
