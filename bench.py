@@ -590,8 +590,9 @@ def copy_calibration():
 def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
     of `bench.py --copy-calibration` into HBM bytes per Full indexer call.
-    head: whether the call runs the decode kernels (index_head + index_select);
-    by default, whether the workload has fewer than four queries per sequence."""
+    head: whether the call scores one query per workgroup (index_head; else the
+    shared-load index_shared_head), then index_select; by default, whether the
+    workload has fewer than four queries per sequence."""
     import csv
     import hashlib
 
@@ -607,10 +608,9 @@ def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
         # the calibration copies are the last three device copies of the run
         return acc, [v for _, v in sorted(copies)[-3:]]
 
-    # the kernels of one Full call.  Decode (one to three queries per sequence):
-    # index_head and index_select, Full instantiations (<false>; the select
-    # grid of the Full call is the larger: it also builds the pool).  More
-    # queries: score, filter (only the Full call launches it) and final.
+    # the kernels of one Full call: a head kernel and the Full call's
+    # index_select (<false, ...>; with a pool its grid is the larger, as it
+    # also builds the pool)
     def full_call(acc, name, largest_grid=False):
         grids = [g for (n, g) in acc if name in n]
         return [v for (n, g), vals in acc.items()
@@ -618,11 +618,8 @@ def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
 
     if head is None:
         head = next(w for w in synth.WORKLOADS.values() if w["name"] == workload_name).get("Q", 1) < 4
-    if head:
-        parts = (("head", "index_head_kernel<false>", False), ("select", "index_select_kernel<false, csa2::SelAll>", True))
-    else:
-        parts = (("score", "index_scoreq_kernel<", False), ("filter", "index_filter_kernel", False),
-                 ("final", "index_final_kernel", True))
+    parts = (("head", "index_head_kernel<false>" if head else "index_shared_head_kernel<", False),
+             ("select", "index_select_kernel<false,", True))
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc, copy = per_kernel(path, counter)
@@ -637,7 +634,7 @@ def summarize_counters(fetch_csv, write_csv, workload_name, head=None):
     for key in ("fetch", "write"):
         kib = sum(out[f"{key}_kib_{part}"] or 0.0 for part, _, _ in parts)
         tot += kib * 1024.0 * out[f"{key}_factor"]
-    src = "index_head.hip" if head else "index.hip"
+    src = "index_head.hip"
     sha = hashlib.sha256(open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", src), "rb").read()).hexdigest()
     out.update(source=src, source_sha256=sha, workload=workload_name, hbm_bytes_per_launch=round(tot))
     path = os.path.join(ROOT, "profiles", f"counters_index_full_{workload_name}.json")
@@ -854,10 +851,8 @@ def main():
     traffic = traffic_from_profiles(wl, "index_full")
     if getattr(wl, "Q", 1) < 4:
         kernel_name = "index_head + index_select (one csa2_index_score_topk Full call)"
-    elif "full_pool" not in getattr(wl, "group", ()):
-        kernel_name = "index_shared_head + index_select (one csa2_index_score_topk Full call)"
     else:
-        kernel_name = "index_scoreq + index_filter + index_final (one csa2_index_score_topk Full call)"
+        kernel_name = "index_shared_head + index_select (one csa2_index_score_topk Full call)"
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_GBPS * 1e9)  # FLOP per byte where the bf16 matrix cores take over
     if flops / idx_bytes < ridge:
         # decode (one or a few queries per sequence): bound by streaming the indexer keys

@@ -17,7 +17,7 @@ static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int64_t kMaxCapacity = 2048LL * csa2::kFullChunk;  // chunk lists one merge accepts
+using csa2::kMaxCapacity;
 constexpr int32_t kMaxRatio = 16;                              // tokens per compressed entry
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -83,8 +83,7 @@ int device_scratch(void* stream, void** out) {
 // GPU.
 int device_status(void* stream) {
   const hipStream_t s = (hipStream_t)stream;
-  const uint32_t e = csa2::take_append_dev_error(s) | csa2::take_index_dev_error(s) | csa2::take_attend_dev_error(s) |
-                     csa2::take_head_dev_error(s);
+  const uint32_t e = csa2::take_append_dev_error(s) | csa2::take_attend_dev_error(s) | csa2::take_head_dev_error(s);
   return e ? CSA2_EDEVICE : CSA2_OK;
 }
 

@@ -474,17 +474,19 @@ struct SharedHeadArgs {
   HeadWs ws;
 };
 
-template <int G>
+template <int G, bool Blocks>
 __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(SharedHeadArgs a) {
   constexpr int kQ = 4 * G;                 // queries per workgroup
   constexpr int kJ = kScoreThreads / 256;  // queries whose elements one pass of the workgroup loads
+  constexpr int kKinds = Blocks ? 2 : 1;    // entries; the pool's 8-entry block maxima
+  constexpr int kSlots = kSharedIters * kBatch;  // (batch, group) pairs of a lane
   static_assert(kQ % kJ == 0 && kQ <= kScoreWaves, "whole passes; one wave per query's cut");
-  __shared__ uint32_t s_hist[kQ][kBins / 2];
+  __shared__ uint32_t s_hist[kKinds][kQ][kBins / 2];
   __shared__ __attribute__((aligned(16))) uint8_t s_q8[kQ][256];
   __shared__ float s_c[kQ][4];
-  __shared__ uint32_t s_max[kQ], s_cut[kQ];
-  __shared__ uint32_t s_n[kQ];
-  __shared__ unsigned long long s_floor[kQ];
+  __shared__ uint32_t s_max[kQ], s_cut[kKinds][kQ];
+  __shared__ uint32_t s_n[kKinds][kQ];
+  __shared__ unsigned long long s_floor[kKinds][kQ];
 
   const int j = blockIdx.y, W = a.W, Q = a.Q;
   const int groups_per_seq = (Q + kQ - 1) / kQ;
@@ -548,11 +550,14 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   if (live(0)) issue(0, bytes[0], sk[0]);
   if (live(1)) issue(1, bytes[1], sk[1]);
 
-  for (int i = tid; i < kQ * kBins / 2; i += kScoreThreads) (&s_hist[0][0])[i] = 0u;
+  for (int i = tid; i < kKinds * kQ * kBins / 2; i += kScoreThreads) (&s_hist[0][0][0])[i] = 0u;
   if (tid < kQ) {
     s_max[tid] = 0u;
-    s_n[tid] = 0u;
-    s_floor[tid] = 0ull;
+#pragma unroll
+    for (int kind = 0; kind < kKinds; kind++) {
+      s_n[kind][tid] = 0u;
+      s_floor[kind][tid] = 0ull;
+    }
   }
 #pragma unroll
   for (int k = 0; k < kQ / kJ; k++) {
@@ -586,9 +591,17 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   }
 
   uint32_t ks[kSharedIters][kBatch][G];  // this lane's keys: batch, group, query 4g + jq
-  uint32_t kmax[G];
+  // block keys: the maximum of (batch it, group jj)'s 8-entry block of this
+  // lane's row is kept by the lane of the block with row % 8 == s % 8, s = 4 it
+  // + jj, in kb[g][s / 8] (four registers for 32 blocks)
+  uint32_t kb[G][Blocks ? kSlots / 8 : 1];
+  uint32_t kmax[G];  // the largest entry key, also the largest block key
 #pragma unroll
-  for (int g = 0; g < G; g++) kmax[g] = 0u;
+  for (int g = 0; g < G; g++) {
+    kmax[g] = 0u;
+#pragma unroll
+    for (int s8 = 0; s8 < (Blocks ? kSlots / 8 : 1); s8++) kb[g][s8] = 0u;
+  }
 #pragma unroll
   for (int it = 0; it < kSharedIters; it++) {
 #pragma unroll
@@ -623,7 +636,14 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
         ks[it][jj][g] = key;
         kmax[g] = max(kmax[g], key);
         const uint32_t bin = key >> kBinShift;
-        atomicAdd(&s_hist[4 * g + jq][bin >> 1], key ? 1u << (16 * (bin & 1u)) : 0u);  // 0: no key, adds nothing
+        atomicAdd(&s_hist[0][4 * g + jq][bin >> 1], key ? 1u << (16 * (bin & 1u)) : 0u);  // 0: no key, adds nothing
+        if constexpr (Blocks) {
+          const uint32_t m = block_max8(key);  // every lane of the block's 8
+          const int sl = it * kBatch + jj;  // a constant once the loops unroll
+          if ((row & 7) == (sl & 7)) kb[g][sl >> 3] = m;
+          const uint32_t bb = m >> kBinShift;
+          if ((row & 7) == 0 && m) atomicAdd(&s_hist[1][4 * g + jq][bb >> 1], 1u << (16 * (bb & 1u)));
+        }
       }
     }
   }
@@ -633,76 +653,125 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   }
   __syncthreads();  // the histograms, maxima and counts are complete
 
-  // wave u finds query u's cut: the bin holding the share's T-th key, with T in
-  // proportion to the share's keys among the query's visible entries
+  // wave u finds query u's cuts: the bin holding the share's T-th key of each
+  // kind, with T in proportion to the share's keys among the query's (its
+  // visible entries, or their blocks, among the share's batches)
   if (wave < nq) {  // uniform
     int32_t total = 0;
 #pragma unroll
     for (int u = 0; u < kQ; u++) total = u == wave ? nv[u] : total;
-    // the share's keys of the query: its visible entries among the share's batches
-    uint32_t lv = 0u;
-    for (int it = 0; it < a.iters; it++) {
-      const int64_t left = (int64_t)total - base_of(it);
-      lv += left <= 0 ? 0u : (left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys);
+#pragma unroll
+    for (int kind = 0; kind < kKinds; kind++) {
+      uint32_t lv = 0u;
+      for (int it = 0; it < a.iters; it++) {
+        const int64_t left = (int64_t)total - base_of(it);
+        const uint32_t ne = left <= 0 ? 0u : (left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys);
+        lv += kind ? (ne + kBlock - 1) / kBlock : ne;
+      }
+      const int64_t K = kind ? kPoolBlocks : kTopK;
+      const int64_t tot = kind ? ((int64_t)total + kBlock - 1) / kBlock : (int64_t)total;
+      const int64_t want = tot > 0 ? (5 * K * lv + 4 * tot - 1) / (4 * tot) + 16 : 0;
+      const int T = (int)min(want, (int64_t)a.T_cap);
+      const uint32_t* h = s_hist[kind][wave];
+      const uint32_t cut =
+          head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
+      if (lane == 0) s_cut[kind][wave] = cut;
     }
-    const int64_t want = total > 0 ? (5 * (int64_t)kTopK * lv + 4 * (int64_t)total - 1) / (4 * (int64_t)total) + 16 : 0;
-    const int T = (int)min(want, (int64_t)a.T_cap);
-    const uint32_t* h = s_hist[wave];
-    const uint32_t cut = head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
-    if (lane == 0) s_cut[wave] = cut;
   }
   __syncthreads();
 
   // each query's keys above its cut to its stretch j; the largest other key is
   // its floor.  A key x is written iff x >= thr (head_written as one compare:
   // thr is the cut bin's lowest key when that bin is written, else the next
-  // bin's, and at least 1); ids ascend with (it, jj) in a lane, so the first
+  // bin's, and at least 1); ids ascend with a lane's (it, jj), so the first
   // unwritten key of the largest value has the lowest id.
+  auto threshold = [](uint32_t cut, bool& any) -> uint32_t {
+    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
+    any = thr64 <= 0xFFFFFFFFull;  // not past the top bin
+    return thr64 > 1ull ? (uint32_t)thr64 : 1u;
+  };
 #pragma unroll
   for (int g = 0; g < G; g++) {
     const int jx = 4 * g + jq;
     if (jx >= nq) continue;
-    const uint32_t cut = s_cut[jx];
-    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
-    const bool any = thr64 <= 0xFFFFFFFFull;  // not past the top bin
-    const uint32_t thr = thr64 > 1ull ? (uint32_t)thr64 : 1u;
-    uint32_t mine = 0u, fx = 0u, fid = 0u;
+    uint64_t* cand = a.ws.cand + ((bq0 + jx) * 2) * kHeadCap + (int64_t)j * a.T_cap;
+    {  // entries
+      bool any;
+      const uint32_t thr = threshold(s_cut[0][jx], any);
+      uint32_t mine = 0u, fx = 0u, fid = 0u;
 #pragma unroll
-    for (int it = 0; it < kSharedIters; it++) {
-      const uint32_t sb = (uint32_t)base_of(it);
+      for (int it = 0; it < kSharedIters; it++) {
+        const uint32_t sb = (uint32_t)base_of(it);
 #pragma unroll
-      for (int jj = 0; jj < kBatch; jj++) {
-        const uint32_t x = ks[it][jj][g];
+        for (int jj = 0; jj < kBatch; jj++) {
+          const uint32_t x = ks[it][jj][g];
+          const bool w = any && x >= thr;
+          mine += w ? 1u : 0u;
+          const uint32_t xu = w ? 0u : x;
+          const bool up = xu > fx;
+          fx = up ? xu : fx;
+          fid = up ? sb + loff[jj] : fid;
+        }
+      }
+      uint32_t slot = atomicAdd(&s_n[0][jx], mine);
+#pragma unroll
+      for (int it = 0; it < kSharedIters; it++) {
+        const uint32_t sb = (uint32_t)base_of(it);
+#pragma unroll
+        for (int jj = 0; jj < kBatch; jj++) {
+          const uint32_t x = ks[it][jj][g];
+          if (any && x >= thr) {
+            if (slot < (uint32_t)a.T_cap) cand[slot] = key64(x, sb + loff[jj]);  // the cap always holds
+            slot++;
+          }
+        }
+      }
+      if (fx) atomicMax(&s_floor[0][jx], (unsigned long long)key64(fx, fid));
+    }
+    if constexpr (Blocks) {  // block maxima: this lane's kb[g][s8] is block slot s = 8 s8 + row % 8
+      bool any;
+      const uint32_t thr = threshold(s_cut[1][jx], any);
+      uint32_t bid[kSlots / 8];
+#pragma unroll
+      for (int s8 = 0; s8 < kSlots / 8; s8++) {
+        const int sl = 8 * s8 + (row & 7);
+        const int it = sl / kBatch, jj = sl % kBatch;
+        const int64_t x = head_batch(j, it, W, a.iters, 0);  // below 2^23 / 512
+        bid[s8] = (uint32_t)((x * kBatchKeys + 16 * (jj * kScoreWaves + wave) + (row & 8)) >> 3);
+      }
+      uint32_t mine = 0u, fx = 0u, fid = 0u;
+#pragma unroll
+      for (int s8 = 0; s8 < kSlots / 8; s8++) {
+        const uint32_t x = kb[g][s8];
         const bool w = any && x >= thr;
         mine += w ? 1u : 0u;
         const uint32_t xu = w ? 0u : x;
         const bool up = xu > fx;
         fx = up ? xu : fx;
-        fid = up ? sb + loff[jj] : fid;
+        fid = up ? bid[s8] : fid;
       }
-    }
-    uint32_t slot = atomicAdd(&s_n[jx], mine);
-    uint64_t* dst = a.ws.cand + ((bq0 + jx) * 2) * kHeadCap + (int64_t)j * a.T_cap;
+      uint32_t slot = atomicAdd(&s_n[1][jx], mine);
+      uint64_t* cb = cand + kHeadCap;
 #pragma unroll
-    for (int it = 0; it < kSharedIters; it++) {
-      const uint32_t sb = (uint32_t)base_of(it);
-#pragma unroll
-      for (int jj = 0; jj < kBatch; jj++) {
-        const uint32_t x = ks[it][jj][g];
+      for (int s8 = 0; s8 < kSlots / 8; s8++) {
+        const uint32_t x = kb[g][s8];
         if (any && x >= thr) {
-          if (slot < (uint32_t)a.T_cap) dst[slot] = key64(x, sb + loff[jj]);  // the cap always holds
+          if (slot < (uint32_t)a.T_cap) cb[slot] = key64(x, bid[s8]);
           slot++;
         }
       }
+      if (fx) atomicMax(&s_floor[1][jx], (unsigned long long)key64(fx, fid));
     }
-    if (fx) atomicMax(&s_floor[jx], (unsigned long long)key64(fx, fid));
   }
   __syncthreads();
   if (tid < nq) {
-    const int64_t sl = ((bq0 + tid) * 2) * a.ws.wstride + j;
-    a.ws.floor[sl] = s_floor[tid];
-    a.ws.cut[sl] = s_cut[tid];
-    a.ws.count[sl] = min(s_n[tid], (uint32_t)a.T_cap);
+#pragma unroll
+    for (int kind = 0; kind < kKinds; kind++) {
+      const int64_t sl = ((bq0 + tid) * 2 + kind) * a.ws.wstride + j;
+      a.ws.floor[sl] = s_floor[kind][tid];
+      a.ws.cut[sl] = s_cut[kind][tid];
+      a.ws.count[sl] = min(s_n[kind][tid], (uint32_t)a.T_cap);
+    }
   }
 }
 
@@ -1590,7 +1659,8 @@ hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq
 // room for one workgroup per compute unit, not two: slower at the
 // 2,048-query prefill.)
 hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, const float* iw, const int32_t* q_pos,
-                                     int32_t* topk_out, int32_t Q, void* ws_head, hipStream_t stream) {
+                                     int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws_head,
+                                     hipStream_t stream) {
   const int64_t bq = (int64_t)c.batch * Q;
   if (bq == 0) return hipSuccess;
   const int qpw = 4;
@@ -1609,15 +1679,19 @@ hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, cons
   h.iters = (int32_t)((batches + h.W - 1) / h.W);  // at most kSharedIters
   // the lean select serves ids below 65,536 (every query's visible entries
   // are at most the capacity)
-  const bool lean = c.capacity <= 32 * SelLean::kBitW;
+  const bool lean = !pool_out && c.capacity <= 32 * SelLean::kBitW;
   int32_t T;
   head_targets(h.W, kTopK, T, h.T_cap, lean ? SelLean::kSet : kHeadCap);
   h.ws = head_ws_carve(ws_head, bq, c.capacity);
   const dim3 grid((unsigned)(c.batch * ((Q + qpw - 1) / qpw)), (unsigned)h.W);
-  hipLaunchKernelGGL(index_shared_head_kernel<1>, grid, dim3(kScoreThreads), 0, stream, h);
+  if (pool_out)
+    hipLaunchKernelGGL((index_shared_head_kernel<1, true>), grid, dim3(kScoreThreads), 0, stream, h);
+  else
+    hipLaunchKernelGGL((index_shared_head_kernel<1, false>), grid, dim3(kScoreThreads), 0, stream, h);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_select(c, false, iq, iw, nullptr, topk_out, nullptr, Q, h.W, h.iters, 0, 0, 1, h.ws, lean, stream);
+  return launch_select(c, false, iq, iw, nullptr, topk_out, pool_out, Q, h.W, h.iters, 0, 0, pool_out ? 2 : 1, h.ws,
+                       lean, stream);
 }
 
 }  // namespace csa2

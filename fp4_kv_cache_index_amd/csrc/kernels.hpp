@@ -19,37 +19,18 @@ struct LaunchCache {
 };
 
 // ---- indexer geometry
-constexpr int kFullChunk = 4096;     // entries scored per workgroup in a Full scan
-constexpr int kReindexChunk = 1024;  // pool slots scored per workgroup in a Reindex scan
+// entries per sequence at most: 2,048 shares of 8 batches of 512 keys, the most
+// shares the select kernel takes
+constexpr int64_t kMaxCapacity = 2048LL * 8 * 512;
 constexpr int kTopK = 512;
 constexpr int kPoolBlocks = 2048;
 constexpr int kBlock = 8;
 constexpr int kPool = kPoolBlocks * kBlock;
 
-inline int64_t full_chunks(int32_t capacity) { return ((int64_t)capacity + kFullChunk - 1) / kFullChunk; }
-inline int64_t reindex_chunks() { return kPool / kReindexChunk; }
-
-// Workspace of one index call.  The first three planes must be zero when a
-// call starts and are left zero when it ends; their offsets depend only on the
-// number of queries, so Full and Reindex calls can share one workspace.
-struct IndexWs {
-  uint32_t* count;  // [BQ][2] candidates found (entries, blocks)
-  uint32_t* fine;   // [BQ][2][256] next 8 bits of the keys in the boundary bin
-  uint32_t* hist;   // [BQ][2][4096] top 12 bits of the score keys
-  uint64_t* cand;   // [BQ][2][8192] candidate u64 keys
-  uint32_t* keys;   // [BQ][slots] score key of every entry (Full) or pool slot (Reindex)
-  uint32_t* bkeys;  // [BQ][slots / 8] block-maximum keys (Full with a pool)
-  int32_t* bound;   // [BQ][2][4] boundary bin, keys above it, all keys (written by the filter)
-  int64_t slots;
-};
-int64_t index_slots(int32_t capacity);
-size_t index_ws_bytes(int64_t bq, int32_t capacity);
-IndexWs index_ws_carve(void* ws, int64_t bq, int32_t capacity);
-// the head path (index_head.hip): one to three queries per sequence, Reindex, and
-// four or more without a pool
+// workspace of an index call (index_head.hip's candidate stretches, counts,
+// floors and cuts); nothing in it carries over between calls
 size_t head_ws_bytes(int64_t bq, int32_t capacity);
 int head_workgroups(bool reindex, int32_t capacity, int64_t bq);
-// the index workspace holds both paths' regions: the shared-load path's first
 size_t index_total_ws_bytes(int64_t bq, int32_t capacity);
 
 // ---- attention geometry
@@ -67,7 +48,6 @@ enum : uint32_t {
   kErrUnreadable = 1u << 31,  // the word itself could not be read or cleared
 };
 uint32_t take_append_dev_error(hipStream_t stream);
-uint32_t take_index_dev_error(hipStream_t stream);
 uint32_t take_attend_dev_error(hipStream_t stream);
 uint32_t take_head_dev_error(hipStream_t stream);
 
@@ -89,10 +69,12 @@ hipError_t launch_index_head(const LaunchCache& c, bool reindex, const float* iq
                              const int32_t* q_pos, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
                              int32_t Q, const float* app_kv, const float* app_ik, int32_t app_T, void* ws_head,
                              hipStream_t stream);
-// Full with four or more queries per sequence and no pool: the shared-load
-// scoring with on-chip candidates, then the same exact selection.
+// Full with four or more queries per sequence: the shared-load scoring with
+// on-chip candidates (and, with pool_out, the pool's block maxima), then the
+// same exact selection.
 hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, const float* iw, const int32_t* q_pos,
-                                     int32_t* topk_out, int32_t Q, void* ws_head, hipStream_t stream);
+                                     int32_t* topk_out, int32_t* pool_out, int32_t Q, void* ws_head,
+                                     hipStream_t stream);
 constexpr int kMaxFusedAppend = 8;  // new entries per sequence an indexing launch appends itself
 hipError_t launch_append_index(const LaunchCache& c, const float* kv, const float* ik, int32_t T, const float* iq,
                                const float* iw, const int32_t* q_pos, int32_t* topk_out, int32_t* pool_out,

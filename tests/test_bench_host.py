@@ -47,9 +47,10 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
 
 
 def test_counter_summary(tmp_path, monkeypatch):
-    """Two synthetic counter CSVs: the last three device copies fix the scale
-    factors, the Full call's final kernel is the one with the larger grid (it
-    also builds the pool), and each kernel's mean per dispatch is scaled."""
+    """Two synthetic counter CSVs of a many-query Full call: the last three
+    device copies fix the scale factors, the Full call's select is the one with
+    the larger grid (it also builds the pool), a Reindex call's kernels are left
+    out, and each kernel's mean per dispatch is scaled."""
     import bench
     fields = "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
 
@@ -57,19 +58,19 @@ def test_counter_summary(tmp_path, monkeypatch):
         return fields + "".join(f'{i},"{k}",{g},{counter},{v}\n' for i, (k, g, v) in enumerate(values))
 
     copy = "__amd_rocclr_copyBuffer"
+    head = "void csa2::index_shared_head_kernel<1, true>(csa2::SharedHeadArgs)"
+    sel = "void csa2::index_select_kernel<false, csa2::SelAll>(csa2::SelectArgs)"
     fetch = [(copy, 4096, 999.0),  # an earlier copy: not a calibration copy
-             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 70000.0),
-             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 70002.0),
-             ("csa2::index_filter_kernel(...)", 131072, 5000.0),
-             ("csa2::index_final_kernel(...)", 16384, 600.0),     # the Full call's (kinds x queries)
-             ("csa2::index_final_kernel(...)", 8192, 12345.0),    # a Reindex call's: left out
-             ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 777.0),
+             (head, 270336, 70000.0),
+             (head, 270336, 70002.0),
+             (sel, 49152, 600.0),     # the Full call's (queries x kinds)
+             ("void csa2::index_head_kernel<true>(csa2::HeadArgs)", 131072, 777.0),  # Reindex: left out
+             ("void csa2::index_select_kernel<true, csa2::SelAll>(csa2::SelectArgs)", 24576, 12345.0),
              (copy, 65536, 131072.0), (copy, 65536, 131072.0), (copy, 65536, 131072.0)]
     write = [(copy, 4096, 999.0),
-             ("void csa2::index_scoreq_kernel<2, true, 1024>(csa2::ScoreqArgs)", 270336, 9500.0),
-             ("csa2::index_filter_kernel(...)", 131072, 600.0),
-             ("csa2::index_final_kernel(...)", 16384, 1600.0),
-             ("csa2::index_final_kernel(...)", 8192, 54321.0),
+             (head, 270336, 9500.0),
+             (sel, 49152, 1600.0),
+             ("void csa2::index_select_kernel<true, csa2::SelAll>(csa2::SelectArgs)", 24576, 54321.0),
              (copy, 65536, 262144.0), (copy, 65536, 262144.0), (copy, 65536, 262144.0)]
     f = tmp_path / "fetch.csv"
     w = tmp_path / "write.csv"
@@ -77,15 +78,15 @@ def test_counter_summary(tmp_path, monkeypatch):
     w.write_text(rows("WRITE_SIZE", write))
     (tmp_path / "profiles").mkdir()
     (tmp_path / "fp4_kv_cache_index_amd" / "csrc").mkdir(parents=True)
-    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index.hip").write_bytes(b"// source\n")
+    (tmp_path / "fp4_kv_cache_index_amd" / "csrc" / "index_head.hip").write_bytes(b"// source\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     bench.summarize_counters(str(f), str(w), "wl_test", head=False)
     out = json.load(open(tmp_path / "profiles" / "counters_index_full_wl_test.json"))
     assert abs(out["fetch_factor"] - 2.0) < 1e-12 and abs(out["write_factor"] - 1.0) < 1e-12
-    assert out["fetch_kib_score"] == 70001.0 and out["fetch_kib_final"] == 600.0
-    want = ((70001.0 + 5000.0 + 600.0) * 2.0 + (9500.0 + 600.0 + 1600.0)) * 1024
+    assert out["fetch_kib_head"] == 70001.0 and out["fetch_kib_select"] == 600.0
+    want = ((70001.0 + 600.0) * 2.0 + (9500.0 + 1600.0)) * 1024
     assert out["hbm_bytes_per_launch"] == round(want)
-    assert out["source"] == "index.hip" and len(out["source_sha256"]) == 64
+    assert out["source"] == "index_head.hip" and len(out["source_sha256"]) == 64
 
 
 def test_counter_summary_decode_kernels(tmp_path, monkeypatch):

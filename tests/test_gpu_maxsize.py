@@ -1,9 +1,9 @@
 """Parity at the largest capacity the library accepts: 2^23 entries per sequence.
 
 At this size the ordering of the selected ids runs with exactly its maximum
-number of buckets (2,048: entries >> 12, blocks >> 9), the filter runs 1,024
-slices per query for the entries and 128 for the pool blocks, and byte offsets
-into the main-KV planes of a second sequence pass 2^32.
+number of buckets (2,048: entries >> 12, blocks >> 9), the select kernel takes
+its most shares per query (2,048 stretches of a few candidates each), and byte
+offsets into the main-KV planes of a second sequence pass 2^32.
 
 The oracle needs minutes to quantise and scan 2^23 rows, so the checks use what
 holds at any size, plus samples the oracle computes one by one:

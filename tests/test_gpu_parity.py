@@ -244,7 +244,7 @@ def test_index_full_ragged_batch_slots(csa, orc):
     print(f"ragged batch slots: boundary swaps {swaps}")
 
 
-@pytest.mark.parametrize("Q", [1, 6])  # the one-query scorer / the eight-query scorer
+@pytest.mark.parametrize("Q", [1, 6])  # the one-query head kernel / the shared-load head kernel
 def test_index_empty_sequences(csa, orc, Q):
     """Sequences with no entry, and queries placed before the first entry, get
     an all -1 Top-K and pool; their neighbour with entries is unaffected; and
@@ -422,8 +422,8 @@ def test_index_shared_heads_relu_zero_ties(csa, orc, E):
         assert np.array_equal(topk[0, q], np.arange(512)), q
 
 
-# selection inside the final kernel / entries through the filter kernel / 8,750 tied pool blocks, more
-# than the candidate buffer holds, selected inside the final kernel
+# 9,000 to 70,000 entries, every score tied (at 70,000, 8,750 tied pool blocks, more than the
+# candidate lists hold): every share whose floor ties S* is re-scored
 @pytest.mark.parametrize("E", [9000, 40000, 70000])
 def test_index_relu_zero_ties_exact(csa, orc, E):
     """Every score is 0: all keys tie in one histogram bin, more than any
@@ -574,7 +574,7 @@ def test_index_reindex(csa, orc, E):
         assert set(got[b, 0].tolist()) == set(ref_full[b, 0].tolist())
 
 
-@pytest.mark.parametrize("Q,pool", [(1, True), (6, True), (6, False)])  # one-query / eight-query scorer
+@pytest.mark.parametrize("Q,pool", [(1, True), (6, True), (6, False)])  # one-query / shared-load head kernel
 def test_index_deterministic(csa, orc, Q, pool):
     """Repeated calls give identical Top-K lists and pools, although every
     path writes its candidates in an order set by atomics."""
