@@ -60,6 +60,7 @@ struct HeadWs {
   uint64_t* cand;   // [BQ][2][kHeadCap] u64 keys (score << 32 | ~id)
   uint64_t* floor;  // [BQ][2][wstride] largest key a workgroup did not write (0: none)
   uint32_t* cut;    // [BQ][2][wstride] its cut bin << 1 | whether that bin was written
+  uint32_t* top;    // [BQ][2][wstride] its largest key (every key it wrote is at most this)
   int32_t* nvis;    // [BQ][2] entries visible to the query; length to store after a fused append (-1: none)
   int32_t wstride;
 };
@@ -102,7 +103,7 @@ static inline int head_wmax(int32_t capacity, int64_t bq) {
 size_t head_ws_bytes(int64_t bq, int32_t capacity) {
   const int64_t W = head_wmax(capacity, bq);
   return 256 + align256(bq * 2 * W * 4) + align256(bq * 2 * kHeadCap * 8) + align256(bq * 2 * W * 8) +
-         align256(bq * 2 * W * 4) + align256(bq * 2 * 4);
+         2 * align256(bq * 2 * W * 4) + align256(bq * 2 * 4);
 }
 
 HeadWs head_ws_carve(void* ws, int64_t bq, int32_t capacity) {
@@ -116,6 +117,8 @@ HeadWs head_ws_carve(void* ws, int64_t bq, int32_t capacity) {
   w.floor = (uint64_t*)p;
   p += align256(bq * 2 * W * 8);
   w.cut = (uint32_t*)p;
+  p += align256(bq * 2 * W * 4);
+  w.top = (uint32_t*)p;
   p += align256(bq * 2 * W * 4);
   w.nvis = (int32_t*)p;
   w.wstride = (int32_t)W;
@@ -137,10 +140,18 @@ __device__ __forceinline__ bool head_written(uint32_t x, uint32_t cut) {
   const uint32_t bn = x >> kBinShift, bt = cut >> 1;
   return x != 0u && (bn > bt || (bn == bt && (cut & 1u)));
 }
+// head_written as one compare: a key x is written iff x >= the threshold (the
+// cut bin's lowest key when that bin is written, else the next bin's, and at
+// least 1) and `any` (false when that is past the top bin)
+__device__ __forceinline__ uint32_t head_threshold(uint32_t cut, bool& any) {
+  const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
+  any = thr64 <= 0xFFFFFFFFull;
+  return thr64 > 1ull ? (uint32_t)thr64 : 1u;
+}
 
 struct HeadLds {
   uint32_t wmax[2][kScoreWaves];    // largest key of each wave, per kind
-  uint32_t cut[2];
+  uint32_t cut[2], top[2];
   int n[2];                         // keys written, per kind (zero before write_heads)
   uint32_t wlive[2][kScoreWaves];   // each wave's nonzero keys, per kind
   uint64_t wfloor[2][kScoreWaves];  // largest key each wave does not write, per kind
@@ -177,8 +188,8 @@ __device__ uint32_t head_cut(CountF count_of, uint32_t mx, int T, int T_cap) {
 
 // Write a share's heads of `kinds` kinds (0: entries or pool slots, 1: block
 // maxima) to its own stretch of the query's candidate list (slots
-// [j T_cap, j T_cap + count) of each kind), with the count, the cut and the
-// floor: the largest key it did not write.  ks[kind][it]: this lane's key of
+// [j T_cap, j T_cap + count) of each kind), with the count, the cut, the
+// share's largest key and the floor: the largest key it did not write.  ks[kind][it]: this lane's key of
 // batch it (0 = none; a block key is held by lane 8b of its block only);
 // idf(kind, it): the key's id.  H.wmax and H.wlive hold every wave's largest
 // key and count of keys, and H.n is zero (the caller has synchronised after the
@@ -191,7 +202,7 @@ template <int kIters, typename IdF>
 __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf, const uint32_t* hist0,
                             const uint32_t* hist1, const int64_t (&total)[2], const int32_t (&T_cap)[2], int j,
                             uint64_t* cand, uint32_t* count_out, uint64_t* floor_out, uint32_t* cut_out,
-                            int32_t stride, HeadLds& H) {
+                            uint32_t* top_out, int32_t stride, HeadLds& H) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int kind = 0; kind < 2; kind++) {
@@ -208,12 +219,8 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     const int T = (int)min(want, (int64_t)T_cap[kind]);
     const uint32_t* hist = kind ? hist1 : hist0;
     const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
-    // head_written as one compare: a key x is written iff x >= thr (the cut
-    // bin's lowest key when that bin is written, else the next bin's, and at
-    // least 1); nothing is written when that is past the top bin
-    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
-    const bool any = thr64 <= 0xFFFFFFFFull;
-    const uint32_t thr = thr64 > 1ull ? (uint32_t)thr64 : 1u;
+    bool any;
+    const uint32_t thr = head_threshold(cut, any);
     // this lane's written keys and the largest unwritten one (the lowest id
     // among equal keys), kept as a 32-bit key and its id
     uint32_t mine = 0u, fx = 0u, fid = 0xFFFFFFFFu;
@@ -241,7 +248,10 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     }
     fl = wave_max(fl);
     if (lane == 0) H.wfloor[kind][wave] = fl;
-    if (tid == 0) H.cut[kind] = cut;
+    if (tid == 0) {
+      H.cut[kind] = cut;
+      H.top[kind] = mx;
+    }
   }
   __syncthreads();
   if (tid < kinds) {
@@ -251,6 +261,7 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     for (int w = 0; w < kScoreWaves; w++) f = max(f, H.wfloor[kind][w]);
     floor_out[kind * stride] = f;
     cut_out[kind * stride] = H.cut[kind];
+    top_out[kind * stride] = H.top[kind];
     count_out[kind * stride] = min((uint32_t)H.n[kind], (uint32_t)T_cap[kind]);
   }
 }
@@ -448,7 +459,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   const int64_t total[2] = {Reindex ? min((int64_t)n_vis, (int64_t)kPool) : (int64_t)n_vis,
                             ((int64_t)n_vis + kBlock - 1) / kBlock};
   write_heads<kIters>(ks, kinds, idf, s_hist, s_bhist, total, a.T_cap, j, a.ws.cand + (bq * 2) * kHeadCap,
-                      a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.wstride, H);
+                      a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.top + sl, a.ws.wstride, H);
 }
 
 // ------------------------------------------------------------------ shared-load heads
@@ -681,15 +692,9 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   __syncthreads();
 
   // each query's keys above its cut to its stretch j; the largest other key is
-  // its floor.  A key x is written iff x >= thr (head_written as one compare:
-  // thr is the cut bin's lowest key when that bin is written, else the next
-  // bin's, and at least 1); ids ascend with a lane's (it, jj), so the first
-  // unwritten key of the largest value has the lowest id.
-  auto threshold = [](uint32_t cut, bool& any) -> uint32_t {
-    const uint64_t thr64 = (uint64_t)((cut >> 1) + ((cut & 1u) ? 0u : 1u)) << kBinShift;
-    any = thr64 <= 0xFFFFFFFFull;  // not past the top bin
-    return thr64 > 1ull ? (uint32_t)thr64 : 1u;
-  };
+  // its floor.  A key x is written iff x >= head_threshold(cut); ids ascend
+  // with a lane's (it, jj), so the first unwritten key of the largest value has
+  // the lowest id.
 #pragma unroll
   for (int g = 0; g < G; g++) {
     const int jx = 4 * g + jq;
@@ -697,7 +702,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
     uint64_t* cand = a.ws.cand + ((bq0 + jx) * 2) * kHeadCap + (int64_t)j * a.T_cap;
     {  // entries
       bool any;
-      const uint32_t thr = threshold(s_cut[0][jx], any);
+      const uint32_t thr = head_threshold(s_cut[0][jx], any);
       uint32_t mine = 0u, fx = 0u, fid = 0u;
 #pragma unroll
       for (int it = 0; it < kSharedIters; it++) {
@@ -730,7 +735,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
     }
     if constexpr (Blocks) {  // block maxima: this lane's kb[g][s8] is block slot s = 8 s8 + row % 8
       bool any;
-      const uint32_t thr = threshold(s_cut[1][jx], any);
+      const uint32_t thr = head_threshold(s_cut[1][jx], any);
       uint32_t bid[kSlots / 8];
 #pragma unroll
       for (int s8 = 0; s8 < kSlots / 8; s8++) {
@@ -770,6 +775,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
       const int64_t sl = ((bq0 + tid) * 2 + kind) * a.ws.wstride + j;
       a.ws.floor[sl] = s_floor[kind][tid];
       a.ws.cut[sl] = s_cut[kind][tid];
+      a.ws.top[sl] = s_max[tid];  // the block keys' largest is the same key
       a.ws.count[sl] = min(s_n[kind][tid], (uint32_t)a.T_cap);
     }
   }
@@ -932,29 +938,37 @@ __device__ __forceinline__ void key_range(Lds& L, int n, uint32_t& lo, uint32_t&
   __syncthreads();
 }
 
+// Bin of a score key x in [lo, hi]: (x - lo) >> bin_shift(lo, hi), below kBins.
+__device__ __forceinline__ int bin_shift(uint32_t lo, uint32_t hi) {
+  const uint32_t span = hi - lo;
+  return span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 12));
+}
+
 // The K-th largest S* of the n unique nonzero u64 keys in L.set (n > K),
 // whose score keys lie in [lo, hi]; with `mark`, also the bit of every key at
-// or above S* in L.bits (the key's id).  On entry L.hist and L.n_tie are zero
-// (and L.bits with `mark`); the call leaves them dirty.  The keys are counted
+// or above S* in L.bits (the key's id).  On entry L.n_tie is zero, and L.hist
+// is zero or, with `counted`, already holds the keys' counts per bin (and
+// L.bits is zero with `mark`); the call leaves them dirty.  The keys are counted
 // in 4,096 bins spanning [lo, hi]; a count over the bins from the top finds the
 // bin holding the K-th key; the keys of higher bins are taken, and that bin's
 // keys (typically one or two) are gathered and ranked exactly (by one wave when
 // there are at most 64 of them, else by the radix select).  Every thread gets
 // S*.
 template <class Lds>
-__device__ __forceinline__ uint64_t select_kth(Lds& L, int n, int K, uint32_t lo, uint32_t hi, bool mark) {
+__device__ __forceinline__ uint64_t select_kth(Lds& L, int n, int K, uint32_t lo, uint32_t hi, bool mark,
+                                              bool counted = false) {
   using C = typename Lds::Cfg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kThr = kScoreThreads;
-  // bin of a score key: (x - lo) >> shift, with (hi - lo) >> shift below kBins
-  const uint32_t span = hi - lo;
-  const int shift = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 12));
-  with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
+  const int shift = bin_shift(lo, hi);
+  if (!counted) {  // uniform
+    with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
 #pragma unroll
-    for (int r = 0; r < b.kN; r++)
-      if (b.x[r]) atomicAdd(&L.hist[(((uint32_t)(b.x[r] >> 32)) - lo) >> shift], 1u);
-  });
-  __syncthreads();
+      for (int r = 0; r < b.kN; r++)
+        if (b.x[r]) atomicAdd(&L.hist[(((uint32_t)(b.x[r] >> 32)) - lo) >> shift], 1u);
+    });
+    __syncthreads();
+  }
   {
     // thread t counts bins [8c, 8c + 8) with c = kThr - 1 - t, so a prefix over
     // the threads is a count from the top bin down; the thread whose range
@@ -1115,68 +1129,94 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   const uint32_t* counts = a.ws.count + (bq * 2 + kind) * a.ws.wstride;
   const uint64_t* floors = a.ws.floor + (bq * 2 + kind) * a.ws.wstride;
   const uint32_t* cuts = a.ws.cut + (bq * 2 + kind) * a.ws.wstride;
+  const uint32_t* tops = a.ws.top + (bq * 2 + kind) * a.ws.wstride;
   // ids of the output: entries or blocks (Full), pool slots (Reindex)
   const int64_t universe = Reindex ? (int64_t)kPool : (kind == 0 ? (int64_t)n_vis : ((int64_t)n_vis + kBlock - 1) / kBlock);
   const bool direct = !C::kWide || universe <= 32 * (int64_t)C::kBitW;  // uniform: the bitmap output
   const int nw = direct ? (int)((universe + 31) >> 5) : 0;
 
-  // ---- the first R slots of every stretch (speculatively), the counts and the
-  // floors, all at once: thread t holds slot pairs p = t + 512 u (pair p is
-  // slots 2 (p mod R/2) and one more of stretch p div R/2), counts and floors of
-  // shares t + 512 f (W <= C::kIdx)
+  // ---- the first R slots of every stretch (speculatively), the counts, floors,
+  // cuts and tops, all at once: thread t holds slot pairs p = t + 512 u (pair p
+  // is slots 2 (p mod R/2) and one more of stretch p div R/2), and the figures
+  // of shares t + 512 f (W <= C::kIdx).  The written keys lie between the
+  // lowest threshold and the largest top of the shares that wrote, so they are
+  // counted in the histogram as they go to L.set.
   constexpr int kPairs = (C::kSet / 2 + kThr - 1) / kThr;  // W tc <= C::kSet
+  static_assert(kPairs >= 4, "the gather's instances");
   constexpr int kFl = C::kIdx / kThr;
   const int R = a.spec[kind], rh = R >> 1;
   const uint32_t rh_magic = a.spec_magic[kind];
   const uint32_t npairs = (uint32_t)W * (uint32_t)rh;
-  const BufRsrc cand_r = make_rsrc(cand, (uint32_t)W * (uint32_t)tc * 8u);
-  uint4 cv[kPairs];
-#pragma unroll
-  for (int u = 0; u < kPairs; u++) {
-    const uint32_t pp = (uint32_t)(tid + u * kThr);
-    const uint32_t sh = __umulhi(pp, rh_magic);
-    const uint32_t s0 = sh * (uint32_t)tc + 2u * (pp - sh * (uint32_t)rh);
-    cv[u] = buf_load16(cand_r, pp < npairs ? 8u * s0 : 0x80000000u);  // past the end: zeros, no access
-  }
-  const BufRsrc cn_r = make_rsrc(counts, (uint32_t)W * 4u);
-  const BufRsrc fl_r = make_rsrc(floors, (uint32_t)W * 8u);
-  uint32_t cn[kFl];
   uint64_t fl[kFl];
+  // NP slot pairs per thread: the least of 2, 4, 6 and kPairs that covers the
+  // speculative slots (uniform), so the loop does no work past them
+  auto gather = [&](auto np_tag) {
+    constexpr int NP = decltype(np_tag)::value;
+    const BufRsrc cand_r = make_rsrc(cand, (uint32_t)W * (uint32_t)tc * 8u);
+    uint4 cv[NP];
 #pragma unroll
-  for (int f = 0; f < kFl; f++) {
-    cn[f] = __builtin_amdgcn_raw_buffer_load_b32(cn_r, 4u * (uint32_t)(tid + f * kThr), 0, 0);
-    fl[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(fl_r, 8u * (uint32_t)(tid + f * kThr), 0, 0));
-  }
-  // the histogram and the bitmap start clear
-  for (int i = tid; i < kBins; i += kThr) L.hist[i] = 0u;
-  for (int i = tid; i < bw(nw); i += kThr) L.bits[i] = 0u;
-  uint64_t fmax = 0ull;
-  bool over = false;
+    for (int u = 0; u < NP; u++) {
+      const uint32_t pp = (uint32_t)(tid + u * kThr);
+      const uint32_t sh = __umulhi(pp, rh_magic);
+      const uint32_t s0 = sh * (uint32_t)tc + 2u * (pp - sh * (uint32_t)rh);
+      cv[u] = buf_load16(cand_r, pp < npairs ? 8u * s0 : 0x80000000u);  // past the end: zeros, no access
+    }
+    const BufRsrc cn_r = make_rsrc(counts, (uint32_t)W * 4u);
+    const BufRsrc fl_r = make_rsrc(floors, (uint32_t)W * 8u);
+    const BufRsrc ct_r = make_rsrc(cuts, (uint32_t)W * 4u);
+    const BufRsrc tp_r = make_rsrc(tops, (uint32_t)W * 4u);
+    uint32_t cn[kFl], ct[kFl], tp[kFl];
 #pragma unroll
-  for (int f = 0; f < kFl; f++) {
-    if (tid + f * kThr < W) L.idx[tid + f * kThr] = cn[f];
-    fmax = max(fmax, fl[f]);
-    over = over || (int)cn[f] > R;  // zero past W
-  }
-  fmax = wave_max(fmax);
-  const bool wover = __ballot(over) != 0ull;
-  if (lane == 0) {
-    L.wfm[wave] = fmax;
-    L.wov[wave] = wover ? 1 : 0;
-  }
-  if (tid == 0) {
-    L.n = 0;
-    L.n_tie = 0;
-  }
-  __syncthreads();
-  // ---- the written slots into L.set, with the range of their score keys
-  {
-    uint64_t k[2 * kPairs];
-    bool v[2 * kPairs];
-    int nv = 0;
+    for (int f = 0; f < kFl; f++) {
+      const uint32_t sj = (uint32_t)(tid + f * kThr);
+      cn[f] = __builtin_amdgcn_raw_buffer_load_b32(cn_r, 4u * sj, 0, 0);
+      fl[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(fl_r, 8u * sj, 0, 0));
+      ct[f] = __builtin_amdgcn_raw_buffer_load_b32(ct_r, 4u * sj, 0, 0);
+      tp[f] = __builtin_amdgcn_raw_buffer_load_b32(tp_r, 4u * sj, 0, 0);
+    }
+    // the histogram and the bitmap start clear
+    for (int i = tid; i < kBins; i += kThr) L.hist[i] = 0u;
+    for (int i = tid; i < bw(nw); i += kThr) L.bits[i] = 0u;
+    uint64_t fmax = 0ull;
+    bool over = false;
     uint32_t lo = ~0u, hi = 0u;
 #pragma unroll
-    for (int u = 0; u < kPairs; u++) {
+    for (int f = 0; f < kFl; f++) {
+      if (tid + f * kThr < W) L.idx[tid + f * kThr] = cn[f];
+      fmax = max(fmax, fl[f]);
+      over = over || (int)cn[f] > R;  // zero past W
+      bool any;
+      const uint32_t thr = head_threshold(ct[f], any);
+      lo = cn[f] ? min(lo, thr) : lo;
+      hi = cn[f] ? max(hi, tp[f]) : hi;
+    }
+    fmax = wave_max(fmax);
+    const bool wover = __ballot(over) != 0ull;
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      L.wfm[wave] = fmax;
+      L.wov[wave] = wover ? 1 : 0;
+      L.wmx[wave] = hi;
+      L.wmn[wave] = lo;
+    }
+    if (tid == 0) {
+      L.n = 0;
+      L.n_tie = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kScoreWaves; w++) {
+      lo = min(lo, L.wmn[w]);
+      hi = max(hi, L.wmx[w]);
+    }
+    const int shift = bin_shift(lo, hi);
+    // ---- the written slots into L.set, each counted in its bin
+    uint64_t k[2 * NP];
+    bool v[2 * NP];
+    int nv = 0;
+#pragma unroll
+    for (int u = 0; u < NP; u++) {
       const uint32_t pp = (uint32_t)(tid + u * kThr);
       const uint32_t sh = __umulhi(pp, rh_magic);
       const int o = 2 * (int)(pp - sh * (uint32_t)rh);  // the pair's first slot in its stretch
@@ -1185,18 +1225,18 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
       v[2 * u + 1] = o + 1 < c;
       k[2 * u] = ((uint64_t)cv[u].y << 32) | cv[u].x;
       k[2 * u + 1] = ((uint64_t)cv[u].w << 32) | cv[u].z;
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const uint32_t x = (uint32_t)(k[2 * u + h] >> 32);
-        nv += v[2 * u + h] ? 1 : 0;
-        lo = v[2 * u + h] ? min(lo, x) : lo;
-        hi = v[2 * u + h] ? max(hi, x) : hi;
-      }
+      nv += (v[2 * u] ? 1 : 0) + (v[2 * u + 1] ? 1 : 0);
     }
+    // every lane stores every key, the unwritten ones to its own spare slot in
+    // L.out (free until the selection); the written ones are counted
     int slot = wave_alloc(nv, &L.n);
 #pragma unroll
-    for (int i = 0; i < 2 * kPairs; i++)
-      if (v[i]) L.set[slot++] = k[i];
+    for (int i = 0; i < 2 * NP; i++) {
+      uint64_t* dst = v[i] ? &L.set[slot] : &L.out[lane];
+      *dst = k[i];
+      slot += v[i] ? 1 : 0;
+      if (v[i]) atomicAdd(&L.hist[(((uint32_t)(k[i] >> 32)) - lo) >> shift], 1u);
+    }
     // stretches holding more than R keys: the rest, one wave per stretch
     bool any_over = false;
 #pragma unroll
@@ -1210,20 +1250,22 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
           const int so = wave_slot(has, &L.n);
           if (has) {
             L.set[so] = x;
-            lo = min(lo, (uint32_t)(x >> 32));
-            hi = max(hi, (uint32_t)(x >> 32));
+            atomicAdd(&L.hist[(((uint32_t)(x >> 32)) - lo) >> shift], 1u);
           }
         }
       }
     }
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lane == 0) {
-      L.wmx[wave] = hi;
-      L.wmn[wave] = lo;
-    }
-  }
-  __syncthreads();
+    __syncthreads();
+  };
+  const uint32_t np = (npairs + kThr - 1) / kThr;  // uniform
+  if (np <= 2)
+    gather(IntC<2>{});
+  else if (np <= 4)
+    gather(IntC<4>{});
+  else if (kPairs > 6 && np <= 6)
+    gather(IntC<6>{});
+  else
+    gather(IntC<kPairs>{});
   int n = L.n;
   uint32_t lo = ~0u, hi = 0u;
   uint64_t gfmax = 0ull;
@@ -1249,7 +1291,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
     }
   }
   // S* = 0 when every candidate is taken
-  uint64_t s_star = n > K ? select_kth(L, n, K, lo, hi, direct) : 0ull;
+  uint64_t s_star = n > K ? select_kth(L, n, K, lo, hi, direct, true) : 0ull;
   bool marked = n > K;  // the bitmap holds the selection
 
   // ---- while a floor is above S*, repair the share with the largest and select again
