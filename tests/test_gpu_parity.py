@@ -344,7 +344,7 @@ def test_index_full_prefill_chunk_no_pool(csa, orc):
             topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"topk b{b} q{q}")
 
 
-@pytest.mark.parametrize("Q", [4, 6, 9])  # one workgroup of four queries / of eight (six used) / eight and one
+@pytest.mark.parametrize("Q", [4, 6, 9])  # workgroups of four queries: one / four and two / two and one
 def test_index_shared_heads_causal(csa, orc, Q):
     """Four or more queries per sequence without a pool: the queries of a
     workgroup share its key loads and keep their keys on chip.  Causal
@@ -371,6 +371,31 @@ def test_index_shared_heads_causal(csa, orc, Q):
             else:
                 swaps += topk_swaps(topk[b, q], ref_topk[b, q], scores[b, q], name=f"b{b} q{q}")
     print(f"shared heads, {Q} queries: boundary swaps {swaps}")
+
+
+@pytest.mark.parametrize("Q", [5, 8])  # two workgroups of four (one used once / both full), with block keys
+def test_index_shared_heads_pool(csa, orc, Q):
+    """Five to eight queries per sequence share their workgroups' key loads,
+    with the pool: causal positions, ragged lengths, per-query head weights;
+    the Top-512 and the pool of every query against the oracle."""
+    B, cap = 3, 40000
+    lengths = [40000, 23117, 9001]
+    oc = oracle_cache_ik(orc, B, cap, lengths, 34)
+    q_pos = np.zeros((B, Q), np.int32)
+    for b in range(B):
+        q_pos[b] = lengths[b] - 1 - np.arange(Q)[::-1] * 997  # spread over the last 7,000 tokens
+    iq = synth.normal(34, f"iq{Q}", (B, Q, 4, 64))
+    iw = synth.uniform(34, f"iw{Q}", (B, Q, 4), 0.25, 2.0)
+    ref, ref_pool, scores = orc.index_topk(oc, orc.FULL, iq, iw=iw, q_pos=q_pos, want_pool=True, want_scores=True)
+    gc = upload(csa, oc)
+    topk, pool = run_full(csa, gc, iq, q_pos=q_pos, iw=iw)
+    swaps = 0
+    for b in range(B):
+        for q in range(Q):
+            n_vis = min(lengths[b], int(q_pos[b, q]) + 1)
+            swaps += topk_swaps(topk[b, q], ref[b, q], scores[b, q], name=f"b{b} q{q}")
+            pool_block_swaps(pool[b, q], ref_pool[b, q], scores[b, q], n_vis, name=f"pool b{b} q{q}")
+    print(f"shared heads with pool, {Q} queries: boundary swaps {swaps}")
 
 
 @pytest.mark.parametrize("lo,n_hot", [(0, 700), (30000, 2000), (61440, 4)])
@@ -404,12 +429,12 @@ def test_index_shared_heads_repair(csa, orc, lo, n_hot):
     print(f"shared heads clustered {lo}+{n_hot}: {swaps} boundary swaps")
 
 
-@pytest.mark.parametrize("E", [9000, 70000])
-def test_index_shared_heads_relu_zero_ties(csa, orc, E):
-    """Every score of four queries is 0: each share's keys all tie in one bin,
-    more than it may write, so every share is re-scored and the lowest
-    entries win."""
-    B, Q = 1, 4
+@pytest.mark.parametrize("E,Q", [(9000, 4), (70000, 4), (70000, 8)])
+def test_index_shared_heads_relu_zero_ties(csa, orc, E, Q):
+    """Every score of four (eight) queries is 0: each share's keys all tie in
+    one bin, more than it may write, so every share is re-scored and the
+    lowest entries win."""
+    B = 1
     oc = orc.Cache(B, E, 1)
     k = np.abs(synth.normal_rows(33, "pos", 0, E, 64)) + 0.1
     oc.ik_codes[0], oc.ik_scales[0] = orc.quantize_ik(k)
