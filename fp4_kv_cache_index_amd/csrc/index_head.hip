@@ -149,6 +149,17 @@ __device__ __forceinline__ uint32_t head_threshold(uint32_t cut, bool& any) {
   return thr64 > 1ull ? (uint32_t)thr64 : 1u;
 }
 
+// Keys a share wants of a kind: 1.25 K live / total + 16, rounded up (0 when
+// the query has no key of the kind), through an fp32 reciprocal rather than an
+// integer division: K live and total are below 2^24, so exact in fp32, and
+// the target needs no exact rounding (the floors keep the selection exact
+// whatever a share writes).
+__device__ __forceinline__ int share_want(int K, uint32_t live, int64_t total) {
+  if (total <= 0) return 0;
+  const float x = 1.25f * (float)K * (float)live * __builtin_amdgcn_rcpf((float)total);
+  return (int)ceilf(x) + 16;
+}
+
 struct HeadLds {
   uint32_t wmax[2][kScoreWaves];    // largest key of each wave, per kind
   uint32_t cut[2], top[2];
@@ -189,15 +200,15 @@ __device__ uint32_t head_cut(CountF count_of, uint32_t mx, int T, int T_cap) {
 // Write a share's heads of `kinds` kinds (0: entries or pool slots, 1: block
 // maxima) to its own stretch of the query's candidate list (slots
 // [j T_cap, j T_cap + count) of each kind), with the count, the cut, the
-// share's largest key and the floor: the largest key it did not write.  ks[kind][it]: this lane's key of
-// batch it (0 = none; a block key is held by lane 8b of its block only);
-// idf(kind, it): the key's id.  H.wmax and H.wlive hold every wave's largest
-// key and count of keys, and H.n is zero (the caller has synchronised after the
-// histograms).  The share wants T = 1.25 K live / total + 16 keys of a kind:
-// a quarter more than its share of the K selected, in proportion to its keys
-// among the query's `total` (a Reindex pool shorter than its slots leaves most
-// shares empty); T_cap: most keys a share may write.  Out-pointers are kind
-// 0's; kind 1's follow at `stride`.
+// share's largest key and the floor: the largest key it did not write.
+// ks[kind][it]: this lane's key of batch it (0 = none; a block key is held by
+// lane 8b of its block only); idf(kind, it): the key's id.  H.wmax and H.wlive
+// hold every wave's largest key and count of keys, and H.n is zero (the caller
+// has synchronised after the histograms).  The share wants T = 1.25 K live /
+// total + 16 keys of a kind (share_want): a quarter more than its share of the
+// K selected, in proportion to its keys among the query's `total` (a Reindex
+// pool shorter than its slots leaves most shares empty); T_cap: most keys a
+// share may write.  Out-pointers are kind 0's; kind 1's follow at `stride`.
 template <int kIters, typename IdF>
 __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf, const uint32_t* hist0,
                             const uint32_t* hist1, const int64_t (&total)[2], const int32_t (&T_cap)[2], int j,
@@ -214,9 +225,7 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
       mx = max(mx, H.wmax[kind][w]);
       live += H.wlive[kind][w];
     }
-    const int64_t K = kind ? kPoolBlocks : kTopK;
-    const int64_t want = total[kind] > 0 ? (5 * K * live + 4 * total[kind] - 1) / (4 * total[kind]) + 16 : 0;
-    const int T = (int)min(want, (int64_t)T_cap[kind]);
+    const int T = min(share_want(kind ? kPoolBlocks : kTopK, live, total[kind]), T_cap[kind]);
     const uint32_t* hist = kind ? hist1 : hist0;
     const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
     bool any;
@@ -315,9 +324,19 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   __shared__ float s_c[4];
   __shared__ HeadLds H;
 
-  const int64_t bq = blockIdx.x;
-  const int j = blockIdx.y;
   const int Q = a.Q, W = a.W;
+  int64_t bq = blockIdx.x;
+  int j = blockIdx.y;
+  if (Q > 1) {  // uniform
+    // the queries of one sequence's share j read the same keys (Full) or
+    // overlapping ones (Reindex over the pools of consecutive tokens): they
+    // take consecutive ranks of one XCD, so that they run side by side over
+    // its L2 (placement only)
+    const int64_t r = xcd_rank((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
+    const int64_t u = r / Q;  // (sequence, share)
+    j = (int)(u % W);
+    bq = (u / W) * Q + r % Q;
+  }
   const int b = (int)(bq / Q), q = (int)(bq % Q);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the query element and head weight this thread quantises (threads 0-255),
@@ -499,9 +518,14 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   __shared__ uint32_t s_n[kKinds][kQ];
   __shared__ unsigned long long s_floor[kKinds][kQ];
 
-  const int j = blockIdx.y, W = a.W, Q = a.Q;
+  const int W = a.W, Q = a.Q;
   const int groups_per_seq = (Q + kQ - 1) / kQ;
-  const int b = (int)(blockIdx.x / groups_per_seq), q0 = (int)(blockIdx.x % groups_per_seq) * kQ;
+  // The query groups of one (sequence, share) read the same keys: they take
+  // consecutive ranks of one XCD, so that they run side by side and the later
+  // ones find the lines in that XCD's L2 (placement only)
+  const int64_t r = xcd_rank(blockIdx.x, gridDim.x);
+  const int64_t u = r / groups_per_seq;
+  const int j = (int)(u % W), b = (int)(u / W), q0 = (int)(r % groups_per_seq) * kQ;
   const int nq = min(kQ, Q - q0);
   const int64_t bq0 = (int64_t)b * Q + q0;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -679,10 +703,8 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
         const uint32_t ne = left <= 0 ? 0u : (left < kBatchKeys ? (uint32_t)left : (uint32_t)kBatchKeys);
         lv += kind ? (ne + kBlock - 1) / kBlock : ne;
       }
-      const int64_t K = kind ? kPoolBlocks : kTopK;
       const int64_t tot = kind ? ((int64_t)total + kBlock - 1) / kBlock : (int64_t)total;
-      const int64_t want = tot > 0 ? (5 * K * lv + 4 * tot - 1) / (4 * tot) + 16 : 0;
-      const int T = (int)min(want, (int64_t)a.T_cap);
+      const int T = min(share_want(kind ? kPoolBlocks : kTopK, lv, tot), (int)a.T_cap);
       const uint32_t* h = s_hist[kind][wave];
       const uint32_t cut =
           head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
@@ -1725,7 +1747,7 @@ hipError_t launch_index_shared_heads(const LaunchCache& c, const float* iq, cons
   int32_t T;
   head_targets(h.W, kTopK, T, h.T_cap, lean ? SelLean::kSet : kHeadCap);
   h.ws = head_ws_carve(ws_head, bq, c.capacity);
-  const dim3 grid((unsigned)(c.batch * ((Q + qpw - 1) / qpw)), (unsigned)h.W);
+  const dim3 grid((unsigned)((int64_t)c.batch * ((Q + qpw - 1) / qpw) * h.W));
   if (pool_out)
     hipLaunchKernelGGL((index_shared_head_kernel<1, true>), grid, dim3(kScoreThreads), 0, stream, h);
   else
