@@ -408,14 +408,16 @@ __device__ __forceinline__ void attend_block(const Wg& w, int j, int grp, const 
   const float m_new = fmaxf(m_run, mx);
   const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
   float ps = 0.0f;
-  v8h pb[2];
+  v8h pb[2], pr[2];  // P as its fp16 rounding and the residual (P_hi + P_lo)
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float pv = sv[kb][i] == -INFINITY ? 0.0f : __expf(sv[kb][i] - m_new);
       ps += pv;
-      pb[kb][i] = (_Float16)pv;
+      const _Float16 ph = (_Float16)pv;
+      pb[kb][i] = ph;
+      pr[kb][i] = (_Float16)(pv - (float)ph);  // the difference is exact in fp32
     }
   ps = rows_sum(ps);
   m_run = m_new;
@@ -433,19 +435,25 @@ __device__ __forceinline__ void attend_block(const Wg& w, int j, int grp, const 
       const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
       const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pr[kb], acc[c], 0, 0, 0);
     }
   }
 }
 
 constexpr int kPStride = 72;  // fp16 per head row of the shared P tile (64 keys + pad)
+constexpr float kLazyMax = 8.0f;  // most a logit may exceed its head's running max (attend_block_sp)
 
 // attend_block with the block's softmax split over the waves (many queries:
 // two workgroups per compute unit, where VALU work, not a barrier, sets the
 // pace): wave w takes heads 4w .. 4w+3, four keys per lane, and shares P (fp16)
 // and each head's rescale factor through LDS (s_p, s_alpha).  This wave's
 // running (m_run, l_run) are those of head 4 wave + lane / 16; the output
-// rows of this lane's accumulators are head n = lane % 16.  The same values
-// as attend_block, but for the order of each head's sum over a block.
+// rows of this lane's accumulators are head n = lane % 16.  A head's running
+// max moves only when a block's maximum exceeds it by more than kLazyMax, so
+// P stays below e^kLazyMax (about 2,981, well inside fp16) and after the
+// first blocks the rescale of the accumulators is mostly skipped; every
+// quantity stays relative to the same m_run, so the softmax is unchanged but
+// for rounding.
 __device__ __forceinline__ void attend_block_sp(const Wg& w, int j, int grp, const Raw& cur, int32_t id_c,
                                                 const v8h (&qb)[16], float qfac, const uint8_t* s_new, _Float16* s_v,
                                                 float* s_s, _Float16* s_p, float* s_alpha, v4f (&acc)[8], float& m_run,
@@ -483,31 +491,40 @@ __device__ __forceinline__ void attend_block_sp(const Wg& w, int j, int grp, con
     const v4f sv = *reinterpret_cast<const v4f*>(s_s + hs * kSStride + k0);
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = wave_row_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
+    // m_run stays unless this block's maximum is more than kLazyMax above it
+    // (a first finite maximum always moves it off -inf)
+    const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+    const float alpha = m_new == m_run ? 1.0f : __expf(m_run - m_new);
     float ps = 0.0f;
-    v4h pv;
+    v4h pv, pl;  // P as its fp16 rounding and the residual (P_hi + P_lo)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const float e = sv[i] == -INFINITY ? 0.0f : __expf(sv[i] - m_new);
       ps += e;
       pv[i] = (_Float16)e;
+      pl[i] = (_Float16)(e - (float)pv[i]);  // the difference is exact in fp32
     }
     ps = wave_row_reduce(ps, [](float x, float y) { return x + y; });
     m_run = m_new;
     l_run = alpha * l_run + ps;
     *reinterpret_cast<v4h*>(s_p + hs * kPStride + k0) = pv;
+    *reinterpret_cast<v4h*>(s_p + (16 + hs) * kPStride + k0) = pl;
     if ((lane & 15) == 0) s_alpha[hs] = alpha;
   }
   lds_barrier();  // P and every head's rescale factor are in
 
   // ---- O^T = alpha O^T + V^T P^T for channels 128 wave .. +127, head n
   const float alpha_n = s_alpha[n];
-  v8h pb[2];
+  v8h pb[2], pr[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; kb++) pb[kb] = *reinterpret_cast<const v8h*>(s_p + n * kPStride + 32 * kb + 8 * g);
+  for (int kb = 0; kb < 2; kb++) {
+    pb[kb] = *reinterpret_cast<const v8h*>(s_p + n * kPStride + 32 * kb + 8 * g);
+    pr[kb] = *reinterpret_cast<const v8h*>(s_p + (16 + n) * kPStride + 32 * kb + 8 * g);
+  }
+  if (__ballot(alpha_n != 1.0f)) {  // uniform: some head's running max moved
 #pragma unroll
-  for (int c = 0; c < 8; c++) acc[c] *= alpha_n;
+    for (int c = 0; c < 8; c++) acc[c] *= alpha_n;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; kb++) {
     const _Float16* vsrc = s_v + (32 * kb + 8 * g + (n >> 2)) * kVStride + 128 * wave + 4 * (n & 3);
@@ -517,6 +534,7 @@ __device__ __forceinline__ void attend_block_sp(const Wg& w, int j, int grp, con
       const v4h hi = lds_read_tr16(vsrc + 4 * kVStride + 16 * c);
       const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[kb], acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pr[kb], acc[c], 0, 0, 0);
     }
   }
 }
@@ -584,7 +602,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __attribute__((aligned(16))) float s_s[16 * kSStride];              // scores [head][key]
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kFusedAppendMax * 512];
   __shared__ float s_qfac[16];
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[kShareP ? 16 * kPStride : 8];  // P [head][key]
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[kShareP ? 32 * kPStride : 8];  // P [head][key], then its residuals
   __shared__ float s_alpha[16];
   __shared__ float2 s_ml[16];
   const Wg w = make_wg(a, kGpw);

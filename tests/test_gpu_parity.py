@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from parity import attn_close, check_sorted_list, pool_block_swaps, topk_swaps
+from parity import attn_close, attn_close_conditioned, check_sorted_list, pool_block_swaps, topk_swaps
 
 pytestmark = pytest.mark.gpu
 SM = float(np.float32(1.0 / math.sqrt(512.0)))
@@ -874,3 +874,50 @@ def test_magnitude_cases(csa, orc, case):
     mabs, mrel = attn_close(host(out.float()), ref, name=case)
     print(f"magnitudes {case}: {swaps} boundary swaps; attention max abs {mabs:.2e}, max rel {mrel:.2e}, "
           f"largest |ref| {np.abs(ref).max():.1f}")
+
+
+@pytest.mark.parametrize("case", ["bound", "outliers"])
+def test_attend_one_split_magnitudes(csa, orc, case):
+    """More than 1,024 queries take one split of all ten blocks per workgroup.
+    At the pages' magnitudes (rows scaled to max |x| = 22.6; saturating groups
+    up to 4 x 2,688) the logits reach thousands, and some of 17,600 rows have
+    two nearly tied keys whose values cancel: there an fp32 logit's rounding,
+    times the row's sensitivity, can exceed 2e-3 + 1e-2|ref|.  Every element
+    must meet that rule or, where it does not, the rule plus the row's
+    conditioning term (attn_close_conditioned); the bound case needs none."""
+    B, Q, E, S = 1, 1100, 4000, 1280
+    cid = 41
+    cap = E + 3
+    oc = orc.Cache(B, cap, 1)
+    kv = _scaled_rows(cid, f"kv{case}", E, 512, case)
+    oc.kv_codes[0, :E], oc.kv_scales[0, :E] = orc.quantize_main(kv)
+    k = _scaled_rows(cid, f"ik{case}", E, 64, case)
+    oc.ik_codes[0, :E], oc.ik_scales[0, :E] = orc.quantize_ik(k)
+    oc.length[0] = E
+    q_pos = np.array([[E - Q + q for q in range(Q)]], np.int32)
+    iq = synth.normal(cid, f"iq{case}", (B, Q, 4, 64))
+    topk, _, _ = orc.index_topk(oc, orc.FULL, iq, q_pos=q_pos)
+    swa = np.zeros((B, S, 512), np.uint8)
+    x = _scaled_rows(cid, f"swa{case}", E, 512, case)[E - S:].reshape(1, S, 512)
+    orc.swa_append(swa, x, np.array([E], np.int32))
+    qf = bf16_round(_scaled_rows(cid, f"q{case}", B * Q * 16, 512, "observed").reshape(B, Q, 16, 512))
+    ref, ref_lse = orc.attend(oc, topk, swa, qf.float().numpy(), SM, q_pos=q_pos)
+    gc = upload(csa, oc, with_main=True)
+    out = torch.empty((B, Q, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Q, 16), dtype=torch.float32, device="cuda")
+    csa.sparse_attend(gc, dev(topk), dev(swa), qf.cuda(), out, SM, lse=lse, q_pos=dev(q_pos))
+    main = orc.dequant_main(oc.kv_codes[0, :E], oc.kv_scales[0, :E]).astype(np.float64)
+    win = orc.e4m3_decode_array(swa[0]).astype(np.float64)
+    qn = qf.float().numpy().astype(np.float64)
+
+    def row_keys(b, q, h):
+        p = int(q_pos[b, q])
+        keys = np.array([main[i] for i in topk[b, q] if i >= 0] + [win[t % S] for t in range(max(0, p - 127), p + 1)])
+        return keys, keys @ qn[b, q, h] * SM, np.abs(keys) @ np.abs(qn[b, q, h]) * SM
+
+    mabs, n_cond = attn_close_conditioned(host(out.float()), ref, row_keys, name=case)
+    np.testing.assert_allclose(host(lse), ref_lse, rtol=1e-4, atol=1e-4)
+    if case == "bound":
+        assert n_cond == 0
+    print(f"one split, magnitudes {case}: attention max abs {mabs:.2e}; {n_cond} of {ref.size} outputs needed "
+          f"the conditioning term; largest |ref| {np.abs(ref).max():.1f}")
