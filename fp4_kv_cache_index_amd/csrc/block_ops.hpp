@@ -114,7 +114,8 @@ __device__ __forceinline__ int wave_alloc(int count, int* counter) {
 // XCDs round-robin (workgroup L to XCD L mod 8), and each XCD has its own L2.
 // Rank r = (L mod 8) * (n / 8) + L / 8 gives XCD x the consecutive ranks
 // [x n/8, (x+1) n/8), so workgroups of consecutive rank (one query's
-// attention splits or merge heads, its filter slices) share an XCD and its L2.
+// attention splits or merge heads, a sequence's index query groups) share an
+// XCD and its L2.
 // Identity when n is not a multiple of 8.  Placement only: no result depends
 // on it.
 __device__ __forceinline__ int64_t xcd_rank(int64_t L, int64_t n) {

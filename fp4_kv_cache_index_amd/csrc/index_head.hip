@@ -1458,14 +1458,37 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
         // its visible entries (every chosen block is full except possibly the one
         // holding the last visible entry, so block r of the order fills slots
         // 8r .. 8r+7): thread t writes the int4 chunks t + 512 k
+        if (bw(nw) <= 2 * C::kOut) {  // uniform: the word offsets fit in L.out, below L.idx
+          // as the Top-512: each chosen block's rank is the chosen blocks
+          // before its word plus the set bits below it in the word (no loop
+          // over the bits of a word, whose length differs from lane to lane)
 #pragma unroll
-        for (int i = 0; i < N; i++) {
-          uint32_t m = wd[i];
-          while (m) {
-            const int b = __ffs(m) - 1;
-            m &= m - 1u;
-            if (pos < kPoolBlocks) L.idx[pos] = (uint32_t)(32 * (w0 + i) + b);
-            pos++;
+          for (int i = 0; i < N; i++) {
+            if (w0 + i < nw) L.woff[bw(w0 + i)] = (uint32_t)pos;
+            pos += __popc(wd[i]);
+          }
+          __syncthreads();
+          with_keys<std::remove_reference_t<decltype(L)>::Cfg::kSet / kScoreThreads>(L.set, n, [&](auto& b) {
+#pragma unroll
+            for (int r = 0; r < b.kN; r++) {
+              if (b.x[r] && b.x[r] >= s_star) {
+                const uint32_t id = key_id(b.x[r]);
+                const int w = (int)(id >> 5);
+                const int rank = (int)L.woff[bw(w)] + __popc(L.bits[bw(w)] & ((1u << (id & 31u)) - 1u));
+                if (rank < kPoolBlocks) L.idx[rank] = id;
+              }
+            }
+          });
+        } else {
+#pragma unroll
+          for (int i = 0; i < N; i++) {
+            uint32_t m = wd[i];
+            while (m) {
+              const int b = __ffs(m) - 1;
+              m &= m - 1u;
+              if (pos < kPoolBlocks) L.idx[pos] = (uint32_t)(32 * (w0 + i) + b);
+              pos++;
+            }
           }
         }
         __syncthreads();
