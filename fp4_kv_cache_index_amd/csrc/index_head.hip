@@ -61,6 +61,7 @@ struct HeadWs {
   uint64_t* floor;  // [BQ][2][wstride] largest key a workgroup did not write (0: none)
   uint32_t* cut;    // [BQ][2][wstride] its cut bin << 1 | whether that bin was written
   uint32_t* top;    // [BQ][2][wstride] its largest key (every key it wrote is at most this)
+  uint32_t* bot;    // [BQ][2][wstride] the smallest key it wrote (all ones: none)
   int32_t* nvis;    // [BQ][2] entries visible to the query; length to store after a fused append (-1: none)
   int32_t wstride;
 };
@@ -103,7 +104,7 @@ static inline int head_wmax(int32_t capacity, int64_t bq) {
 size_t head_ws_bytes(int64_t bq, int32_t capacity) {
   const int64_t W = head_wmax(capacity, bq);
   return 256 + align256(bq * 2 * W * 4) + align256(bq * 2 * kHeadCap * 8) + align256(bq * 2 * W * 8) +
-         2 * align256(bq * 2 * W * 4) + align256(bq * 2 * 4);
+         3 * align256(bq * 2 * W * 4) + align256(bq * 2 * 4);
 }
 
 HeadWs head_ws_carve(void* ws, int64_t bq, int32_t capacity) {
@@ -119,6 +120,8 @@ HeadWs head_ws_carve(void* ws, int64_t bq, int32_t capacity) {
   w.cut = (uint32_t*)p;
   p += align256(bq * 2 * W * 4);
   w.top = (uint32_t*)p;
+  p += align256(bq * 2 * W * 4);
+  w.bot = (uint32_t*)p;
   p += align256(bq * 2 * W * 4);
   w.nvis = (int32_t*)p;
   w.wstride = (int32_t)W;
@@ -166,6 +169,7 @@ struct HeadLds {
   int n[2];                         // keys written, per kind (zero before write_heads)
   uint32_t wlive[2][kScoreWaves];   // each wave's nonzero keys, per kind
   uint64_t wfloor[2][kScoreWaves];  // largest key each wave does not write, per kind
+  uint32_t wbot[2][kScoreWaves];    // smallest key each wave writes, per kind
 };
 
 // One wave walks a kind's histogram down from the bin of the share's largest
@@ -200,7 +204,8 @@ __device__ uint32_t head_cut(CountF count_of, uint32_t mx, int T, int T_cap) {
 // Write a share's heads of `kinds` kinds (0: entries or pool slots, 1: block
 // maxima) to its own stretch of the query's candidate list (slots
 // [j T_cap, j T_cap + count) of each kind), with the count, the cut, the
-// share's largest key and the floor: the largest key it did not write.
+// share's largest key, the smallest key it wrote and the floor: the largest
+// key it did not write.
 // ks[kind][it]: this lane's key of batch it (0 = none; a block key is held by
 // lane 8b of its block only); idf(kind, it): the key's id.  H.wmax and H.wlive
 // hold every wave's largest key and count of keys, and H.n is zero (the caller
@@ -213,7 +218,7 @@ template <int kIters, typename IdF>
 __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf, const uint32_t* hist0,
                             const uint32_t* hist1, const int64_t (&total)[2], const int32_t (&T_cap)[2], int j,
                             uint64_t* cand, uint32_t* count_out, uint64_t* floor_out, uint32_t* cut_out,
-                            uint32_t* top_out, int32_t stride, HeadLds& H) {
+                            uint32_t* top_out, uint32_t* bot_out, int32_t stride, HeadLds& H) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int kind = 0; kind < 2; kind++) {
@@ -227,17 +232,19 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
     }
     const int T = min(share_want(kind ? kPoolBlocks : kTopK, live, total[kind]), T_cap[kind]);
     const uint32_t* hist = kind ? hist1 : hist0;
-    const uint32_t cut = head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
+    // a share with no more keys than it wants writes them all (no histogram walk)
+    const uint32_t cut = live <= (uint32_t)T ? 1u : head_cut([&](int bn) { return hist[bn]; }, mx, T, T_cap[kind]);
     bool any;
     const uint32_t thr = head_threshold(cut, any);
     // this lane's written keys and the largest unwritten one (the lowest id
     // among equal keys), kept as a 32-bit key and its id
-    uint32_t mine = 0u, fx = 0u, fid = 0xFFFFFFFFu;
+    uint32_t mine = 0u, fx = 0u, fid = 0xFFFFFFFFu, mn = 0xFFFFFFFFu;
 #pragma unroll
     for (int it = 0; it < kIters; it++) {
       const uint32_t x = ks[kind][it];
       const bool w = any && x >= thr;
       mine += w ? 1u : 0u;
+      mn = w ? min(mn, x) : mn;
       const uint32_t xu = w ? 0u : x;
       const uint32_t id = idf(kind, it);
       const bool up = xu > fx || (xu == fx && id < fid);
@@ -256,7 +263,11 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
       slot += w ? 1u : 0u;
     }
     fl = wave_max(fl);
-    if (lane == 0) H.wfloor[kind][wave] = fl;
+    mn = wave_min(mn);
+    if (lane == 0) {
+      H.wfloor[kind][wave] = fl;
+      H.wbot[kind][wave] = mn;
+    }
     if (tid == 0) {
       H.cut[kind] = cut;
       H.top[kind] = mx;
@@ -266,11 +277,16 @@ __device__ void write_heads(const uint32_t (&ks)[2][kIters], int kinds, IdF idf,
   if (tid < kinds) {
     const int kind = tid;
     uint64_t f = 0ull;
+    uint32_t bt = 0xFFFFFFFFu;
 #pragma unroll
-    for (int w = 0; w < kScoreWaves; w++) f = max(f, H.wfloor[kind][w]);
+    for (int w = 0; w < kScoreWaves; w++) {
+      f = max(f, H.wfloor[kind][w]);
+      bt = min(bt, H.wbot[kind][w]);
+    }
     floor_out[kind * stride] = f;
     cut_out[kind * stride] = H.cut[kind];
     top_out[kind * stride] = H.top[kind];
+    bot_out[kind * stride] = bt;
     count_out[kind * stride] = min((uint32_t)H.n[kind], (uint32_t)T_cap[kind]);
   }
 }
@@ -478,7 +494,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_head_kernel(HeadArgs a) {
   const int64_t total[2] = {Reindex ? min((int64_t)n_vis, (int64_t)kPool) : (int64_t)n_vis,
                             ((int64_t)n_vis + kBlock - 1) / kBlock};
   write_heads<kIters>(ks, kinds, idf, s_hist, s_bhist, total, a.T_cap, j, a.ws.cand + (bq * 2) * kHeadCap,
-                      a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.top + sl, a.ws.wstride, H);
+                      a.ws.count + sl, a.ws.floor + sl, a.ws.cut + sl, a.ws.top + sl, a.ws.bot + sl, a.ws.wstride, H);
 }
 
 // ------------------------------------------------------------------ shared-load heads
@@ -514,7 +530,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
   __shared__ uint32_t s_hist[kKinds][kQ][kBins / 2];
   __shared__ __attribute__((aligned(16))) uint8_t s_q8[kQ][256];
   __shared__ float s_c[kQ][4];
-  __shared__ uint32_t s_max[kQ], s_cut[kKinds][kQ];
+  __shared__ uint32_t s_max[kQ], s_cut[kKinds][kQ], s_bot[kKinds][kQ];
   __shared__ uint32_t s_n[kKinds][kQ];
   __shared__ unsigned long long s_floor[kKinds][kQ];
 
@@ -592,6 +608,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
     for (int kind = 0; kind < kKinds; kind++) {
       s_n[kind][tid] = 0u;
       s_floor[kind][tid] = 0ull;
+      s_bot[kind][tid] = 0xFFFFFFFFu;
     }
   }
 #pragma unroll
@@ -706,8 +723,11 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
       const int64_t tot = kind ? ((int64_t)total + kBlock - 1) / kBlock : (int64_t)total;
       const int T = min(share_want(kind ? kPoolBlocks : kTopK, lv, tot), (int)a.T_cap);
       const uint32_t* h = s_hist[kind][wave];
+      // no more keys than it wants (lv counts the visible ones): all written
       const uint32_t cut =
-          head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
+          lv <= (uint32_t)T
+              ? 1u
+              : head_cut([&](int bn) { return (h[bn >> 1] >> (16 * (bn & 1))) & 0xFFFFu; }, s_max[wave], T, a.T_cap);
       if (lane == 0) s_cut[kind][wave] = cut;
     }
   }
@@ -725,7 +745,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
     {  // entries
       bool any;
       const uint32_t thr = head_threshold(s_cut[0][jx], any);
-      uint32_t mine = 0u, fx = 0u, fid = 0u;
+      uint32_t mine = 0u, fx = 0u, fid = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
       for (int it = 0; it < kSharedIters; it++) {
         const uint32_t sb = (uint32_t)base_of(it);
@@ -750,10 +770,12 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
           if (any && x >= thr) {
             if (slot < (uint32_t)a.T_cap) cand[slot] = key64(x, sb + loff[jj]);  // the cap always holds
             slot++;
+            mn = min(mn, x);  // tracked here, not while counting: fewer registers live across the loops
           }
         }
       }
       if (fx) atomicMax(&s_floor[0][jx], (unsigned long long)key64(fx, fid));
+      if (mine) atomicMin(&s_bot[0][jx], mn);
     }
     if constexpr (Blocks) {  // block maxima: this lane's kb[g][s8] is block slot s = 8 s8 + row % 8
       bool any;
@@ -766,7 +788,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
         const int64_t x = head_batch(j, it, W, a.iters, 0);  // below 2^23 / 512
         bid[s8] = (uint32_t)((x * kBatchKeys + 16 * (jj * kScoreWaves + wave) + (row & 8)) >> 3);
       }
-      uint32_t mine = 0u, fx = 0u, fid = 0u;
+      uint32_t mine = 0u, fx = 0u, fid = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
       for (int s8 = 0; s8 < kSlots / 8; s8++) {
         const uint32_t x = kb[g][s8];
@@ -785,9 +807,11 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
         if (any && x >= thr) {
           if (slot < (uint32_t)a.T_cap) cb[slot] = key64(x, bid[s8]);
           slot++;
+          mn = min(mn, x);
         }
       }
       if (fx) atomicMax(&s_floor[1][jx], (unsigned long long)key64(fx, fid));
+      if (mine) atomicMin(&s_bot[1][jx], mn);
     }
   }
   __syncthreads();
@@ -798,6 +822,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_shared_head_kernel(Shared
       a.ws.floor[sl] = s_floor[kind][tid];
       a.ws.cut[sl] = s_cut[kind][tid];
       a.ws.top[sl] = s_max[tid];  // the block keys' largest is the same key
+      a.ws.bot[sl] = s_bot[kind][tid];
       a.ws.count[sl] = min(s_n[kind][tid], (uint32_t)a.T_cap);
     }
   }
@@ -1152,17 +1177,18 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
   const uint64_t* floors = a.ws.floor + (bq * 2 + kind) * a.ws.wstride;
   const uint32_t* cuts = a.ws.cut + (bq * 2 + kind) * a.ws.wstride;
   const uint32_t* tops = a.ws.top + (bq * 2 + kind) * a.ws.wstride;
+  const uint32_t* bots = a.ws.bot + (bq * 2 + kind) * a.ws.wstride;
   // ids of the output: entries or blocks (Full), pool slots (Reindex)
   const int64_t universe = Reindex ? (int64_t)kPool : (kind == 0 ? (int64_t)n_vis : ((int64_t)n_vis + kBlock - 1) / kBlock);
   const bool direct = !C::kWide || universe <= 32 * (int64_t)C::kBitW;  // uniform: the bitmap output
   const int nw = direct ? (int)((universe + 31) >> 5) : 0;
 
   // ---- the first R slots of every stretch (speculatively), the counts, floors,
-  // cuts and tops, all at once: thread t holds slot pairs p = t + 512 u (pair p
-  // is slots 2 (p mod R/2) and one more of stretch p div R/2), and the figures
-  // of shares t + 512 f (W <= C::kIdx).  The written keys lie between the
-  // lowest threshold and the largest top of the shares that wrote, so they are
-  // counted in the histogram as they go to L.set.
+  // bottoms and tops, all at once: thread t holds slot pairs p = t + 512 u
+  // (pair p is slots 2 (p mod R/2) and one more of stretch p div R/2), and the
+  // figures of shares t + 512 f (W <= C::kIdx).  The written keys lie between
+  // the smallest bottom and the largest top of the shares that wrote, so they
+  // are counted in the histogram as they go to L.set.
   constexpr int kPairs = (C::kSet / 2 + kThr - 1) / kThr;  // W tc <= C::kSet
   static_assert(kPairs >= 4, "the gather's instances");
   constexpr int kFl = C::kIdx / kThr;
@@ -1185,15 +1211,15 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
     }
     const BufRsrc cn_r = make_rsrc(counts, (uint32_t)W * 4u);
     const BufRsrc fl_r = make_rsrc(floors, (uint32_t)W * 8u);
-    const BufRsrc ct_r = make_rsrc(cuts, (uint32_t)W * 4u);
+    const BufRsrc bt_r = make_rsrc(bots, (uint32_t)W * 4u);
     const BufRsrc tp_r = make_rsrc(tops, (uint32_t)W * 4u);
-    uint32_t cn[kFl], ct[kFl], tp[kFl];
+    uint32_t cn[kFl], bt[kFl], tp[kFl];
 #pragma unroll
     for (int f = 0; f < kFl; f++) {
       const uint32_t sj = (uint32_t)(tid + f * kThr);
       cn[f] = __builtin_amdgcn_raw_buffer_load_b32(cn_r, 4u * sj, 0, 0);
       fl[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(fl_r, 8u * sj, 0, 0));
-      ct[f] = __builtin_amdgcn_raw_buffer_load_b32(ct_r, 4u * sj, 0, 0);
+      bt[f] = __builtin_amdgcn_raw_buffer_load_b32(bt_r, 4u * sj, 0, 0);
       tp[f] = __builtin_amdgcn_raw_buffer_load_b32(tp_r, 4u * sj, 0, 0);
     }
     // the histogram and the bitmap start clear
@@ -1207,9 +1233,7 @@ __global__ void __launch_bounds__(kScoreThreads) index_select_kernel(SelectArgs 
       if (tid + f * kThr < W) L.idx[tid + f * kThr] = cn[f];
       fmax = max(fmax, fl[f]);
       over = over || (int)cn[f] > R;  // zero past W
-      bool any;
-      const uint32_t thr = head_threshold(ct[f], any);
-      lo = cn[f] ? min(lo, thr) : lo;
+      lo = cn[f] ? min(lo, bt[f]) : lo;
       hi = cn[f] ? max(hi, tp[f]) : hi;
     }
     fmax = wave_max(fmax);
